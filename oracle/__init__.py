@@ -1,0 +1,24 @@
+"""CPU oracle for prefix-tree-packed attention and the Basal decision.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or link
+this package: only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` use it. It shares no code with the HIP library and imports
+nothing from ``prefix_tree_packed_amd``.
+
+It is a plain, slow, obviously correct restatement of what the pages define:
+
+* ``oracle.tree``      index tables and the dense visibility mask of a packed tree
+                       (architecture page, section 03 "Packing", "Attention over
+                       tree blocks"; section 01 "Batch and prefix tree");
+* ``oracle.attention`` dense-mask softmax attention in float64;
+* ``oracle.decision``  the two-order decision and temperature calibration
+                       (architecture page, section 02 "Basal protocol").
+
+"The architecture page" throughout is "How basal-rs computes a decision"
+(basal.itsol.dev/en/architecture), with its Polish version
+(basal.itsol.dev/pl/architektura) used to read garbled passages.
+
+Every function is pinned by ``-m "not gpu"`` tests against the pages' worked
+examples, closed forms, invariants and brute force; none is "parity unpinned".
+"""
+from . import tree, attention, decision  # noqa: F401
