@@ -1,0 +1,236 @@
+"""Throughput of prefix-tree-packed tree attention + the decision epilogue on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--seed 0]
+
+One step = one pass of the device hot path over one batch: for every forward
+of the workload, the chunk's K/V cache write and the tree-attention launch
+(the two launches tree_attn_forward_chunked makes, issued through its two
+halves so the attention launch can be timed on its own), then the decision
+epilogue for the batch. The plan (host validation, token tables, block-sparse
+schedule, upload) is built once per batch before the timed region: it is
+shared by every layer of a model, and its host time is reported as
+plan_build_ms. Inputs are resident in HBM before timing starts.
+
+Prints one JSON line. `value` is useful tree-attention TFLOP/s over the whole
+step (useful FLOPs = 4 * head_dim * q_heads * sum over query tokens of the
+keys each may see); `roofline` is the attention kernel alone, timed with HIP
+events on the launch stream; `cpu_baseline` is the float64 CPU oracle on a
+bounded sample of the same workload (rank 0, one GPU only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2516.6   # MI355X dense f16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--out-dtype", default="f16", choices=["f16", "f32"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                          "(multi-GPU sharding is described in DESIGN.md, not implemented)"}))
+        sys.exit(2)
+
+    import torch
+    import prefix_tree_packed_amd as P
+    from workloads import make_config
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = make_config(args.config, args.seed)
+    stream = torch.cuda.current_stream()
+
+    def T(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---- plans (host) + device inputs -------------------------------------
+    t0 = time.perf_counter()
+    plans = [P.tree_attn_plan(f.tree, wl.hq, wl.hkv, wl.d, wl.scale, out_dtype=args.out_dtype)
+             for f in wl.forwards]
+    plan_build_ms = (time.perf_counter() - t0) * 1e3
+    for p in plans:
+        P.tree_attn_plan_upload(p)
+    infos = [p.info for p in plans]
+    odt = torch.float16 if args.out_dtype == "f16" else torch.float32
+    fw = []
+    shared = wl.notes.get("shared_cache", False)
+    cache = None
+    for f, info in zip(wl.forwards, infos):
+        kn, vn = f.kv_new()
+        if cache is None or not shared:
+            kc, vc = f.cache_before()
+            cache = (T(kc), T(vc))
+            cache0 = (cache[0].clone(), cache[1].clone())
+        fw.append(dict(q=T(f.q), kn=T(kn), vn=T(vn), kc=cache[0], vc=cache[1], kc0=cache0[0],
+                       vc0=cache0[1], o=torch.empty((info["num_q_tokens"], wl.hq, wl.d), dtype=odt,
+                                                   device=dev)))
+    d = wl.decisions
+    logits, row1, row2 = T(d.logits), T(d.row1), T(d.row2)
+    nl, temps = T(d.n_letters), T(d.T)
+    p_avg = torch.empty((d.n_dec, d.logits.shape[1]), dtype=torch.float32, device=dev)
+    p_cal = torch.empty_like(p_avg)
+    torch.cuda.synchronize()
+
+    n_fw = len(fw)
+    ev_a = [[torch.cuda.Event(enable_timing=True) for _ in range(n_fw)] for _ in range(args.steps)]
+    ev_b = [[torch.cuda.Event(enable_timing=True) for _ in range(n_fw)] for _ in range(args.steps)]
+
+    def step(i=None):
+        for j, (p, x) in enumerate(zip(plans, fw)):
+            P.tree_attn_cache_write(p, x["kn"], x["vn"], x["kc"], x["vc"], stream=stream)
+            if i is not None:
+                ev_a[i][j].record(stream)
+            P.tree_attn_forward_cached(p, x["q"], x["kc"], x["vc"], x["o"], stream=stream)
+            if i is not None:
+                ev_b[i][j].record(stream)
+        P.decision_readout(logits, row1, row2, nl, temps, p_avg, p_cal, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    attn_ms = [[ev_a[i][j].elapsed_time(ev_b[i][j]) for j in range(n_fw)] for i in range(args.steps)]
+    attn_ms = np.array(attn_ms)                       # [steps, forwards]
+    attn_ms_mean = attn_ms.mean(axis=0)               # per forward
+
+    useful_pairs = [i["useful_pairs"] for i in infos]
+    useful_flops = [4.0 * wl.d * wl.hq * u for u in useful_pairs]
+    q_tokens = sum(i["num_q_tokens"] for i in infos)
+    value = sum(useful_flops) / (ms_per_step * 1e-3) / 1e12
+    # dominant kernel: the attention launch of the heaviest forward
+    k = int(np.argmax(useful_flops))
+    achieved = useful_flops[k] / (attn_ms_mean[k] * 1e-3) / 1e12
+    attn_total_tflops = sum(useful_flops) / (attn_ms_mean.sum() * 1e-3) / 1e12
+
+    out = {
+        "metric": "useful tree-attention TFLOP/s (packed tokens/s and % of f16 MFMA peak alongside)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "packed_tokens_per_s": round(q_tokens / (ms_per_step * 1e-3), 1),
+        "pct_mfma_peak": round(100 * value / PEAK_F16_TFLOPS, 2),
+        "attention_only_tflops": round(attn_total_tflops, 3),
+        "attention_ms_per_forward": [round(float(x), 5) for x in attn_ms_mean],
+        "plan_build_ms": round(plan_build_ms, 3),
+        "config": {
+            "workload": f"config[{args.config}] {wl.name}",
+            "seed": args.seed,
+            "forwards": n_fw,
+            "q_tokens_per_forward": [i["num_q_tokens"] for i in infos],
+            "kv_tokens_per_forward": [i["num_kv_tokens"] for i in infos],
+            "q_heads": wl.hq, "kv_heads": wl.hkv, "head_dim": wl.d,
+            "useful_gflop_per_step": round(sum(useful_flops) / 1e9, 3),
+            "decisions": d.n_dec,
+            "out_dtype": args.out_dtype,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "tree_attn_fwd_kernel",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+            "traffic": None,
+            "per_launch": {"useful_flop": useful_flops[k], "avg_ms": round(float(attn_ms_mean[k]), 5),
+                           "forward_index": k},
+        },
+    }
+
+    # correctness guard on the timed outputs (cheap): finite everywhere
+    for x in fw:
+        assert torch.isfinite(x["o"].float()).all().item(), "non-finite attention output"
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, infos, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, infos, seconds):
+    """The float64 oracle, as it stands, on a bounded sample of the same
+    workload: query tokens of the heaviest forward in slices of 128 (spread over
+    the forward) until `seconds` of wall time are spent; reported as useful
+    TFLOP/s of the sampled tokens."""
+    from oracle import attention as OA
+    from oracle import tree as OT
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    useful = [i["useful_pairs"] for i in infos]
+    k = int(np.argmax(useful))
+    f = wl.forwards[k]
+    idx = OT.build_index(f.tree)
+    toks = OT.query_tokens(idx)
+    vis = toks["pos_id"].astype(np.int64) + 1
+    nq = len(vis)
+    order = np.random.default_rng(0).permutation(nq)
+    done, pairs = 0, 0
+    t0 = time.perf_counter()
+    while done < nq and time.perf_counter() - t0 < seconds:
+        sel = np.sort(order[done:done + 128])
+        OA.tree_attention(f.tree, f.q, f.k_row, f.v_row, wl.scale, sel=sel)
+        pairs += int(vis[sel].sum())
+        done += len(sel)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * wl.d * wl.hq * pairs
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {nq} query tokens (random, slices of 128) of forward {k}, all "
+                      f"{wl.hq} heads, float64 dense-mask oracle, {dt:.1f} s",
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,261 @@
+/*
+ * tree_attn.h -- C ABI of the prefix-tree-packed attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What it computes comes from the architecture page "How basal-rs computes a
+ * decision" (basal.itsol.dev/en/architecture):
+ *
+ *   - section 01 "Request path", stage "Batch and prefix tree": the prompts of
+ *     a batch are arranged into rows, each row a tree whose shared prefixes are
+ *     computed once; a row holds at most 32,768 tokens, one forward pass
+ *     computes at most 8,192, trees are at most 8 blocks deep;
+ *   - section 03 "Packing", "Attention over tree blocks": before computation a
+ *     tree becomes one row of tokens; a token attends to the earlier tokens of
+ *     its own block and to all tokens of its ancestor blocks, siblings are
+ *     masked, so each token gets what running its full prompt alone gives; its
+ *     RoPE position is its position in its own prompt;
+ *   - section 01, stage "GPU forward pass": the batch runs as one compact f16
+ *     token list without padding, attention accumulates in f32;
+ *   - section 02 "Basal protocol": the two-order decision and its calibration.
+ *
+ * Conventions shared by every call:
+ *   - All functions return a ta_status. On any status other than TA_OK nothing
+ *     has been enqueued on the stream and no output has been written;
+ *     tree_attn_last_error() then returns a message (thread-local, valid until
+ *     the next call on the same thread).
+ *   - Device pointers are HIP device memory of the current device; the caller
+ *     owns every device buffer, including the plan workspace. The library owns
+ *     only the opaque plan's host memory.
+ *   - `hip_stream` is a hipStream_t (NULL = the null stream). Every launch is
+ *     asynchronous on it; no call synchronises the host except
+ *     tree_attn_plan_upload (see there). Faults inside a kernel surface at the
+ *     caller's next synchronisation of the stream.
+ *   - No silent fallback: an unsupported shape returns TA_ERR_LIMIT.
+ *   - f16 is IEEE binary16, f32 IEEE binary32. Token-major layouts:
+ *     Q/O [tokens][heads][head_dim], K/V [tokens][kv_heads][head_dim], each
+ *     dense; every device pointer must be 16-byte aligned.
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ta_plan_s* ta_plan_t; /* opaque; host memory owned by the library */
+
+typedef enum {
+  TA_OK = 0,
+  TA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad head configuration, bad query span,
+                                  misaligned buffer, call not valid for this plan      */
+  TA_ERR_INVALID_TREE = 2,     /* empty row, block length < 1, parent not in [-1, self) */
+  TA_ERR_LIMIT = 3,            /* row > 32768 tokens, forward > 8192 tokens, depth > 8,
+                                  head_dim not 64/128, heads per KV head not 1/2/4/8      */
+  TA_ERR_HIP = 4,              /* a HIP runtime call failed (message has its text)       */
+  TA_ERR_WORKSPACE = 5         /* plan not uploaded, workspace too small or misaligned,
+                                  K/V cache smaller than the plan's row space             */
+} ta_status;
+
+typedef enum { TA_F16 = 0, TA_F32 = 1 } ta_dtype;
+
+/*
+ * A batch's prefix trees, in host memory (read during tree_attn_plan only).
+ *
+ * Row r owns blocks [row_block_indptr[r], row_block_indptr[r+1]) of the block
+ * arrays. block_parent[b] is the parent's index *inside the same row* (0-based
+ * from the row's first block) or -1 for a root; it must be smaller than b's own
+ * index inside the row, so parents come before children. A row may hold several
+ * trees (several -1 roots); tokens of different trees, and of different rows,
+ * never attend to each other. Blocks are laid out in the order given: row token
+ * i belongs to the block whose span [start, start+len) holds i, where each
+ * block starts where the previous block of its row ended.
+ *
+ * Row space: rows are concatenated in order, row r's token i at index
+ * row_base[r] + i with row_base[0] = 0 and row_base[r+1] = row_base[r] +
+ * row length. This forward computes, for each row, tokens [row_q_begin[r],
+ * row_q_end[r]) (NULL arrays mean 0 and the row length). Its query tokens are
+ * numbered in forward order: row 0's span, then row 1's, and so on. Tokens
+ * before row_q_begin[r] are K/V already in the cache (a template computed at
+ * start-up, or earlier chunks of a long row: section 01 "Batch and prefix tree",
+ * section 03 "the template computed once at start-up").
+ */
+typedef struct {
+  int32_t num_rows;                 /* >= 0 */
+  const int32_t* row_block_indptr;  /* [num_rows+1], indptr[0] = 0, each row >= 1 block */
+  const int32_t* block_parent;      /* [indptr[num_rows]] */
+  const int32_t* block_len;         /* [indptr[num_rows]], each >= 1 */
+  const int32_t* row_q_begin;       /* [num_rows] or NULL */
+  const int32_t* row_q_end;         /* [num_rows] or NULL */
+} ta_tree_desc;
+
+/*
+ * Attention shape. Query head h reads KV head h / (num_q_heads / num_kv_heads)
+ * (grouped heads are contiguous). scale multiplies Q.K before the softmax and
+ * must be finite and > 0 (usually 1/sqrt(head_dim)). out_dtype selects the type
+ * of O. write_lse != 0 makes the forwards accept an LSE output.
+ */
+typedef struct {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;   /* 64 or 128 */
+  float scale;
+  ta_dtype out_dtype;
+  int32_t write_lse;
+} ta_attn_cfg;
+
+typedef struct {
+  int64_t num_q_tokens;    /* T_q: tokens this forward computes                          */
+  int64_t num_kv_tokens;   /* row-space size: the K/V cache must hold at least this many */
+  int64_t useful_pairs;    /* sum over query tokens of the keys each may see              */
+  int64_t cost_packed;     /* tokens computed with shared prefixes counted once (= T_q)
+                              (section 01, stage "Validation and planning": request cost) */
+  int64_t cost_separate;   /* tokens all root-to-leaf prompts would cost run one by one   */
+  int32_t num_rows;
+  int32_t num_blocks;
+  int32_t num_leaves;      /* leaves whose last token this forward computes               */
+  int32_t max_depth;       /* blocks on the longest root-to-leaf path                     */
+  int32_t num_q_tiles;     /* query tiles of the block-sparse schedule                    */
+  int32_t num_work_items;  /* query tiles x KV heads: workgroups of one attention launch  */
+  int64_t num_key_tiles;   /* key tiles visited summed over query tiles (one KV head)     */
+  int64_t num_masked_key_tiles;
+  int32_t q_tile_tokens;   /* tokens per query tile                                       */
+  int32_t one_shot;        /* 1 if every row is computed whole (tree_attn_forward valid)  */
+  size_t workspace_bytes;  /* device workspace tree_attn_plan_upload needs                */
+} ta_plan_info;
+
+/*
+ * tree_attn_plan -- validate a batch's trees and build the block-sparse
+ * schedule on the host: per-token tables (row, block, offset in block, RoPE
+ * position = summed ancestor lengths + offset, section 03), query tiles, and
+ * for each query tile the list of key tiles taken from its blocks' ancestor
+ * lists plus its own blocks' causal prefixes, with the tiles that need a mask
+ * flagged. Host only; touches no device. On success *out owns a new plan.
+ * Errors: TA_ERR_INVALID_ARGUMENT, TA_ERR_INVALID_TREE, TA_ERR_LIMIT.
+ */
+ta_status tree_attn_plan(const ta_tree_desc* desc, const ta_attn_cfg* cfg, ta_plan_t* out);
+
+/* Sizes and counts of a plan. Host only. */
+ta_status tree_attn_plan_info(ta_plan_t plan, ta_plan_info* out);
+
+/*
+ * Copy the plan's device tables into caller-owned device memory `d_workspace`
+ * (at least info.workspace_bytes bytes, 256-byte aligned) with an async copy on
+ * `hip_stream`, and remember the workspace for later forwards. The workspace
+ * must stay allocated and unmodified while forwards using this plan run. The
+ * call returns once the host-side tables may be freed (the copy itself is
+ * ordered on the stream). A plan may be uploaded again (e.g. to another
+ * workspace); forwards use the latest upload.
+ * Errors: TA_ERR_INVALID_ARGUMENT, TA_ERR_WORKSPACE, TA_ERR_HIP.
+ */
+ta_status tree_attn_plan_upload(ta_plan_t plan, void* d_workspace, size_t bytes, void* hip_stream);
+
+/*
+ * Host export of the per-token tables, for tests. Each pointer may be NULL.
+ * pos_id, tok_row, tok_block (global block index into the description's block
+ * arrays), tok_offset: [num_q_tokens], in forward order. leaf_block and
+ * leaf_readout_tok: [num_leaves], the leaves (blocks with no children) whose
+ * last token this forward computes, in block order, and that token's forward
+ * index (the readout position, section 01 stage "GPU forward pass").
+ */
+ta_status tree_attn_plan_export(ta_plan_t plan, int32_t* pos_id, int32_t* tok_row,
+                                int32_t* tok_block, int32_t* tok_offset,
+                                int32_t* leaf_block, int32_t* leaf_readout_tok);
+
+/*
+ * Host copy of the block-sparse schedule the attention kernel runs, for tests
+ * and tools. Each pointer may be NULL.
+ *   q_tiles [num_q_tiles * 5]: per query tile (forward index of its first
+ *           token, row-space index of its first token, tokens, first key tile,
+ *           end key tile)
+ *   key_tiles [num_key_tiles * 3]: per key tile (row-space first key, keys,
+ *           1 if the kernel applies the per-key visibility test, else 0)
+ *   work [num_work_items]: launch order, query_tile * num_kv_heads + kv_head
+ *   tok_anc [num_kv_tokens * 2]: per row-space token, the Euler interval
+ *           [tin, tout) of its block over the forest; key u is visible to
+ *           query t iff tin(u) < tin(t) < tout(u), or tin(u) == tin(t) and u <= t
+ */
+ta_status tree_attn_plan_schedule(ta_plan_t plan, int32_t* q_tiles, int32_t* key_tiles,
+                                  int32_t* work, int32_t* tok_anc);
+
+/* Free the plan's host memory. The device workspace stays the caller's. NULL is a no-op. */
+ta_status tree_attn_plan_destroy(ta_plan_t plan);
+
+/*
+ * One-shot tree attention: every row is computed whole (info.one_shot == 1),
+ * so query index == row-space index.
+ *   q   [T_q, Hq, D] f16        k, v [T_q, Hkv, D] f16
+ *   o   [T_q, Hq, D] out_dtype  lse  [Hq, T_q] f32 natural-log sum-exp, or NULL
+ * O[t,h] = sum_u P[t,u] V[u,kv] with P the softmax over the keys u that t may
+ * see of scale * Q[t,h].K[u,kv] (f16 inputs, f32 accumulation and softmax, P
+ * rounded to f16 for the P.V product).
+ * Errors: TA_ERR_INVALID_ARGUMENT (null/misaligned pointer, plan not one-shot,
+ * lse given without write_lse), TA_ERR_WORKSPACE, TA_ERR_HIP.
+ */
+ta_status tree_attn_forward(ta_plan_t plan, const void* q, const void* k, const void* v,
+                            void* o, float* lse, void* hip_stream);
+
+/*
+ * Chunked tree attention against a row-space K/V cache (long rows computed as
+ * forwards of at most 8,192 tokens, and a template cached at start-up).
+ *   q              [T_q, Hq, D] f16, this forward's tokens in forward order
+ *   k_new, v_new   [T_q, Hkv, D] f16, their keys and values
+ *   k_cache, v_cache [cache_tokens, Hkv, D] f16 in row space; on entry rows'
+ *                  tokens before row_q_begin hold their K/V; on return this
+ *                  forward's K/V are also written at their row-space index
+ *   cache_tokens   >= info.num_kv_tokens
+ *   o, lse         as for tree_attn_forward
+ * Two launches on the stream: the cache write, then attention over the cache.
+ * Errors: as tree_attn_forward, plus TA_ERR_WORKSPACE for a short cache.
+ */
+ta_status tree_attn_forward_chunked(ta_plan_t plan, const void* q, const void* k_new,
+                                    const void* v_new, void* k_cache, void* v_cache,
+                                    int64_t cache_tokens, void* o, float* lse, void* hip_stream);
+
+/*
+ * The two halves of tree_attn_forward_chunked, for callers that produce K/V
+ * straight into the cache or want to time the attention launch alone.
+ * tree_attn_cache_write: copy k_new/v_new [T_q, Hkv, D] f16 into the row-space
+ *   cache at each forward token's row-space index (one launch).
+ * tree_attn_forward_cached: attention of this forward's queries over a cache
+ *   that already holds every key they may see, this forward's own included
+ *   (one launch). Arguments and errors as tree_attn_forward_chunked.
+ */
+ta_status tree_attn_cache_write(ta_plan_t plan, const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, int64_t cache_tokens, void* hip_stream);
+ta_status tree_attn_forward_cached(ta_plan_t plan, const void* q, const void* k_cache,
+                                   const void* v_cache, int64_t cache_tokens, void* o, float* lse,
+                                   void* hip_stream);
+
+/*
+ * The Basal decision (section 02 "Basal protocol"), for n_dec questions:
+ *   p     = (softmax(l_order1) + reverse(softmax(l_order2))) / 2
+ *   p_cal = softmax(ln(max(p, 1e-12)) / T)
+ * where order 2 lists the same options in reverse order, so reverse() puts its
+ * probabilities back in the request's option order.
+ *   logits    [n_rows, ld] f32 device   letter logits, one readout per row
+ *   row1,row2 [n_dec] int32 device      decision i's order-1 / order-2 rows
+ *   n_letters [n_dec] int32 device      letters of decision i
+ *   T         [n_dec] f32 device        temperature of decision i
+ *   p_avg, p_cal [n_dec, ld] f32 device outputs, unrounded; columns >= n_letters[i] are 0
+ * Host-checked: pointers non-null, ld >= 2, n_rows >= 1, n_dec >= 0 (0: nothing is
+ * launched). Per-decision values live on the device and are checked by the kernel:
+ * a decision with a row outside [0, n_rows), n_letters outside [2, min(ld, 255)]
+ * (255 = the largest choice question, section 07), or T not a finite positive
+ * number gets NaN in every column of both outputs.
+ * Errors: TA_ERR_INVALID_ARGUMENT, TA_ERR_HIP.
+ */
+ta_status decision_readout(const float* logits, int32_t n_rows, int32_t ld, const int32_t* row1,
+                           const int32_t* row2, const int32_t* n_letters, const float* T,
+                           int32_t n_dec, float* p_avg, float* p_cal, void* hip_stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* tree_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H */

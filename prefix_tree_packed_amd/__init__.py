@@ -1,0 +1,25 @@
+"""Prefix-tree-packed attention and the Basal decision for AMD MI355X (gfx950).
+
+The compute lives in libtreeattn.so (C ABI: include/tree_attn.h): a host plan
+builder and hand-written HIP kernels. ``prefix_tree_packed_amd.binding`` is the
+thin Python binding with the same function names; importing this package does
+not load the library, the first binding call does (and raises if it is missing).
+"""
+
+from .binding import (  # noqa: F401
+    Plan,
+    TreeAttnError,
+    decision_readout,
+    load_library,
+    tree_attn_cache_write,
+    tree_attn_forward,
+    tree_attn_forward_cached,
+    tree_attn_forward_chunked,
+    tree_attn_last_error,
+    tree_attn_plan,
+    tree_attn_plan_destroy,
+    tree_attn_plan_export,
+    tree_attn_plan_info,
+    tree_attn_plan_schedule,
+    tree_attn_plan_upload,
+)

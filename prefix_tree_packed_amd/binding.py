@@ -1,0 +1,314 @@
+"""Python binding of libtreeattn.so (include/tree_attn.h), same names as the C ABI.
+
+Argument marshalling only: every step of the hot path runs in the library's
+host code and HIP kernels. PyTorch provides device memory and the current HIP
+stream. The binding checks tensor dtypes, devices, contiguity and shapes
+against the plan before any pointer reaches the library (the C ABI sees only
+pointers, so this is where a short buffer is caught). There is no fallback: if
+the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtreeattn.so")
+
+TA_OK = 0
+STATUS_NAMES = {0: "TA_OK", 1: "TA_ERR_INVALID_ARGUMENT", 2: "TA_ERR_INVALID_TREE",
+                3: "TA_ERR_LIMIT", 4: "TA_ERR_HIP", 5: "TA_ERR_WORKSPACE"}
+TA_F16, TA_F32 = 0, 1
+
+EXPORTED = ("tree_attn_plan", "tree_attn_plan_info", "tree_attn_plan_upload",
+            "tree_attn_plan_export", "tree_attn_plan_schedule", "tree_attn_plan_destroy", "tree_attn_forward",
+            "tree_attn_forward_chunked", "tree_attn_cache_write", "tree_attn_forward_cached",
+            "decision_readout", "tree_attn_last_error")
+
+
+class TreeAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class _TreeDesc(ctypes.Structure):
+    _fields_ = [("num_rows", ctypes.c_int32),
+                ("row_block_indptr", ctypes.POINTER(ctypes.c_int32)),
+                ("block_parent", ctypes.POINTER(ctypes.c_int32)),
+                ("block_len", ctypes.POINTER(ctypes.c_int32)),
+                ("row_q_begin", ctypes.POINTER(ctypes.c_int32)),
+                ("row_q_end", ctypes.POINTER(ctypes.c_int32))]
+
+
+class _AttnCfg(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("out_dtype", ctypes.c_int), ("write_lse", ctypes.c_int32)]
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [("num_q_tokens", ctypes.c_int64), ("num_kv_tokens", ctypes.c_int64),
+                ("useful_pairs", ctypes.c_int64), ("cost_packed", ctypes.c_int64),
+                ("cost_separate", ctypes.c_int64), ("num_rows", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("num_leaves", ctypes.c_int32),
+                ("max_depth", ctypes.c_int32), ("num_q_tiles", ctypes.c_int32),
+                ("num_work_items", ctypes.c_int32), ("num_key_tiles", ctypes.c_int64),
+                ("num_masked_key_tiles", ctypes.c_int64), ("q_tile_tokens", ctypes.c_int32),
+                ("one_shot", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libtreeattn.so once. torch is imported first so that the library
+    binds to the HIP runtime torch already loaded (one runtime per process)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  (loads torch's HIP runtime before ours)
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m prefix_tree_packed_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    lib.tree_attn_plan.argtypes = [ctypes.POINTER(_TreeDesc), ctypes.POINTER(_AttnCfg), ctypes.POINTER(vp)]
+    lib.tree_attn_plan_info.argtypes = [vp, ctypes.POINTER(_PlanInfo)]
+    lib.tree_attn_plan_upload.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    lib.tree_attn_plan_export.argtypes = [vp, p32, p32, p32, p32, p32, p32]
+    lib.tree_attn_plan_schedule.argtypes = [vp, p32, p32, p32, p32]
+    lib.tree_attn_plan_destroy.argtypes = [vp]
+    lib.tree_attn_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.tree_attn_forward_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, vp, vp]
+    lib.tree_attn_cache_write.argtypes = [vp, vp, vp, vp, vp, i64, vp]
+    lib.tree_attn_forward_cached.argtypes = [vp, vp, vp, vp, i64, vp, vp, vp]
+    lib.decision_readout.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp]
+    for name in EXPORTED[:-1]:
+        getattr(lib, name).restype = ctypes.c_int
+    lib.tree_attn_last_error.restype = ctypes.c_char_p
+    lib.tree_attn_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def tree_attn_last_error() -> str:
+    return load_library().tree_attn_last_error().decode()
+
+
+def _check(status: int):
+    if status != TA_OK:
+        raise TreeAttnError(status, tree_attn_last_error())
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr32(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Plan:
+    """Owns a ta_plan_t; freed by tree_attn_plan_destroy (or on garbage collection)."""
+
+    def __init__(self, handle: int, arrays, cfg: dict):
+        self.handle = ctypes.c_void_p(handle)
+        self._arrays = arrays  # keep host arrays alive for the call's duration
+        self.cfg = cfg
+        self.workspace = None
+        self._info = None
+
+    @property
+    def info(self) -> dict:
+        if self._info is None:
+            self._info = tree_attn_plan_info(self)
+        return self._info
+
+    def __del__(self):
+        try:
+            tree_attn_plan_destroy(self)
+        except Exception:
+            pass
+
+
+def tree_attn_plan(tree, num_q_heads: int, num_kv_heads: int, head_dim: int, scale: float,
+                   out_dtype: str = "f16", write_lse: bool = False) -> Plan:
+    """Build a plan from a tree description (any object with the fields
+    row_block_indptr, block_parent, block_len, row_q_begin, row_q_end)."""
+    lib = load_library()
+    indptr = _i32(tree.row_block_indptr)
+    parent = _i32(tree.block_parent)
+    lens = _i32(tree.block_len)
+    qb = None if getattr(tree, "row_q_begin", None) is None else _i32(tree.row_q_begin)
+    qe = None if getattr(tree, "row_q_end", None) is None else _i32(tree.row_q_end)
+    desc = _TreeDesc(int(indptr.shape[0]) - 1, _ptr32(indptr), _ptr32(parent), _ptr32(lens),
+                     _ptr32(qb), _ptr32(qe))
+    od = {"f16": TA_F16, "f32": TA_F32}[out_dtype]
+    cfg = _AttnCfg(int(num_q_heads), int(num_kv_heads), int(head_dim), float(scale), od,
+                   1 if write_lse else 0)
+    out = ctypes.c_void_p()
+    _check(lib.tree_attn_plan(ctypes.byref(desc), ctypes.byref(cfg), ctypes.byref(out)))
+    return Plan(out.value, (indptr, parent, lens, qb, qe),
+                {"num_q_heads": int(num_q_heads), "num_kv_heads": int(num_kv_heads),
+                 "head_dim": int(head_dim), "scale": float(scale), "out_dtype": out_dtype,
+                 "write_lse": bool(write_lse)})
+
+
+def tree_attn_plan_info(plan: Plan) -> dict:
+    info = _PlanInfo()
+    _check(load_library().tree_attn_plan_info(plan.handle, ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in _PlanInfo._fields_}
+
+
+def tree_attn_plan_upload(plan: Plan, workspace=None, stream=None):
+    """Upload the plan's device tables. Allocates a torch uint8 workspace on the
+    current device when none is given; returns the workspace (kept on the plan)."""
+    import torch
+    need = plan.info["workspace_bytes"]
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().tree_attn_plan_upload(plan.handle, ctypes.c_void_p(workspace.data_ptr()),
+                                                nbytes, _stream_handle(stream)))
+    plan.workspace = workspace
+    return workspace
+
+
+def tree_attn_plan_export(plan: Plan) -> dict:
+    info = plan.info
+    nq, nl = info["num_q_tokens"], info["num_leaves"]
+    out = {k: np.zeros(nq, np.int32) for k in ("pos_id", "tok_row", "tok_block", "tok_offset")}
+    out["leaf_block"] = np.zeros(nl, np.int32)
+    out["leaf_readout_tok"] = np.zeros(nl, np.int32)
+    _check(load_library().tree_attn_plan_export(
+        plan.handle, _ptr32(out["pos_id"]), _ptr32(out["tok_row"]), _ptr32(out["tok_block"]),
+        _ptr32(out["tok_offset"]), _ptr32(out["leaf_block"]), _ptr32(out["leaf_readout_tok"])))
+    return out
+
+
+def tree_attn_plan_schedule(plan: Plan) -> dict:
+    """Host copy of the block-sparse schedule (query tiles, key tiles, launch
+    order, per-token Euler intervals)."""
+    info = plan.info
+    out = {"q_tiles": np.zeros((info["num_q_tiles"], 5), np.int32),
+           "key_tiles": np.zeros((info["num_key_tiles"], 3), np.int32),
+           "work": np.zeros(info["num_work_items"], np.int32),
+           "tok_anc": np.zeros((info["num_kv_tokens"], 2), np.int32)}
+    _check(load_library().tree_attn_plan_schedule(
+        plan.handle, _ptr32(out["q_tiles"]), _ptr32(out["key_tiles"]), _ptr32(out["work"]),
+        _ptr32(out["tok_anc"])))
+    return out
+
+
+def tree_attn_plan_destroy(plan: Plan) -> None:
+    if plan.handle is not None and plan.handle.value:
+        _check(load_library().tree_attn_plan_destroy(plan.handle))
+        plan.handle = ctypes.c_void_p(None)
+
+
+def _expect(t, name, shape, dtype):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _vp(t):
+    return ctypes.c_void_p(None if t is None else t.data_ptr())
+
+
+def _attn_io_checks(plan, q, o, lse):
+    import torch
+    info, cfg = plan.info, plan.cfg
+    nq, hq, hkv, d = info["num_q_tokens"], cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"]
+    _expect(q, "q", (nq, hq, d), torch.float16)
+    _expect(o, "o", (nq, hq, d), torch.float32 if cfg["out_dtype"] == "f32" else torch.float16)
+    if lse is not None:
+        _expect(lse, "lse", (hq, nq), torch.float32)
+    return nq, hkv, d
+
+
+def tree_attn_forward(plan: Plan, q, k, v, o, lse=None, stream=None) -> None:
+    import torch
+    nq, hkv, d = _attn_io_checks(plan, q, o, lse)
+    _expect(k, "k", (nq, hkv, d), torch.float16)
+    _expect(v, "v", (nq, hkv, d), torch.float16)
+    _check(load_library().tree_attn_forward(plan.handle, _vp(q), _vp(k), _vp(v), _vp(o), _vp(lse),
+                                            _stream_handle(stream)))
+
+
+def tree_attn_forward_chunked(plan: Plan, q, k_new, v_new, k_cache, v_cache, o, lse=None,
+                              stream=None) -> None:
+    import torch
+    nq, hkv, d = _attn_io_checks(plan, q, o, lse)
+    _expect(k_new, "k_new", (nq, hkv, d), torch.float16)
+    _expect(v_new, "v_new", (nq, hkv, d), torch.float16)
+    ct = k_cache.shape[0]
+    _expect(k_cache, "k_cache", (ct, hkv, d), torch.float16)
+    _expect(v_cache, "v_cache", (ct, hkv, d), torch.float16)
+    _check(load_library().tree_attn_forward_chunked(
+        plan.handle, _vp(q), _vp(k_new), _vp(v_new), _vp(k_cache), _vp(v_cache), int(ct), _vp(o),
+        _vp(lse), _stream_handle(stream)))
+
+
+def tree_attn_cache_write(plan: Plan, k_new, v_new, k_cache, v_cache, stream=None) -> None:
+    import torch
+    info, cfg = plan.info, plan.cfg
+    nq, hkv, d = info["num_q_tokens"], cfg["num_kv_heads"], cfg["head_dim"]
+    _expect(k_new, "k_new", (nq, hkv, d), torch.float16)
+    _expect(v_new, "v_new", (nq, hkv, d), torch.float16)
+    ct = k_cache.shape[0]
+    _expect(k_cache, "k_cache", (ct, hkv, d), torch.float16)
+    _expect(v_cache, "v_cache", (ct, hkv, d), torch.float16)
+    _check(load_library().tree_attn_cache_write(plan.handle, _vp(k_new), _vp(v_new), _vp(k_cache),
+                                                _vp(v_cache), int(ct), _stream_handle(stream)))
+
+
+def tree_attn_forward_cached(plan: Plan, q, k_cache, v_cache, o, lse=None, stream=None) -> None:
+    import torch
+    nq, hkv, d = _attn_io_checks(plan, q, o, lse)
+    ct = k_cache.shape[0]
+    _expect(k_cache, "k_cache", (ct, hkv, d), torch.float16)
+    _expect(v_cache, "v_cache", (ct, hkv, d), torch.float16)
+    _check(load_library().tree_attn_forward_cached(plan.handle, _vp(q), _vp(k_cache), _vp(v_cache),
+                                                   int(ct), _vp(o), _vp(lse), _stream_handle(stream)))
+
+
+def decision_readout(logits, row1, row2, n_letters, T, p_avg, p_cal, stream=None) -> None:
+    import torch
+    if logits.dim() != 2:
+        raise ValueError("logits must be [n_rows, ld]")
+    n_rows, ld = logits.shape
+    n_dec = row1.shape[0]
+    _expect(logits, "logits", (n_rows, ld), torch.float32)
+    for name, t, dt in (("row1", row1, torch.int32), ("row2", row2, torch.int32),
+                        ("n_letters", n_letters, torch.int32), ("T", T, torch.float32)):
+        _expect(t, name, (n_dec,), dt)
+    _expect(p_avg, "p_avg", (n_dec, ld), torch.float32)
+    _expect(p_cal, "p_cal", (n_dec, ld), torch.float32)
+    _check(load_library().decision_readout(_vp(logits), int(n_rows), int(ld), _vp(row1), _vp(row2),
+                                           _vp(n_letters), _vp(T), int(n_dec), _vp(p_avg), _vp(p_cal),
+                                           _stream_handle(stream)))

@@ -1,0 +1,157 @@
+// C-ABI entry points that touch the device: plan upload, the two attention
+// forwards and the decision epilogue. Every argument is checked before
+// anything is enqueued (include/tree_attn.h states the contract).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace ta {
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static ta_status hip_fail(hipError_t e, const char* what) {
+  return fail(TA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static ta_status check_tensors(ta_plan_t p, const void* const* ptrs, const char* const* names, int n,
+                               float* lse) {
+  if (!p) return fail(TA_ERR_INVALID_ARGUMENT, "NULL plan");
+  if (!p->d_ws) return fail(TA_ERR_WORKSPACE, "plan has not been uploaded");
+  for (int i = 0; i < n; ++i) {
+    if (!ptrs[i]) return fail(TA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(TA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+  }
+  if (lse && !p->cfg.write_lse)
+    return fail(TA_ERR_INVALID_ARGUMENT, "lse given but the plan was built with write_lse = 0");
+  if (lse && ((uintptr_t)lse & 3u)) return fail(TA_ERR_INVALID_ARGUMENT, "lse is not 4-byte aligned");
+  return TA_OK;
+}
+
+static AttnArgs attn_args(ta_plan_t p, const void* q, const void* k, const void* v, void* o, float* lse) {
+  const unsigned char* ws = (const unsigned char*)p->d_ws;
+  AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.qtiles = ws + p->off_qtiles;
+  a.ktiles = ws + p->off_ktiles;
+  a.work = ws + p->off_work;
+  a.tok_anc = ws + p->off_anc;
+  a.hq = p->cfg.num_q_heads;
+  a.hkv = p->cfg.num_kv_heads;
+  a.head_dim = p->cfg.head_dim;
+  a.group = p->group;
+  a.n_q = (int)p->n_q;
+  a.n_work = (int)p->work.size();
+  a.scale_log2e = p->cfg.scale * 1.4426950408889634f;
+  a.out_f32 = p->cfg.out_dtype == TA_F32;
+  return a;
+}
+
+}  // namespace ta
+
+extern "C" {
+
+ta_status tree_attn_plan_upload(ta_plan_t p, void* d_workspace, size_t bytes, void* hip_stream) {
+  ta::clear_error();
+  if (!p || !d_workspace) return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (bytes < p->ws_bytes)
+    return ta::fail(TA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", bytes, p->ws_bytes);
+  if ((uintptr_t)d_workspace & 255u) return ta::fail(TA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  hipError_t e = hipMemcpyAsync(d_workspace, p->image.data(), p->ws_bytes, hipMemcpyHostToDevice,
+                                (hipStream_t)hip_stream);
+  if (e != hipSuccess) return ta::hip_fail(e, "plan upload");
+  p->d_ws = d_workspace;
+  return TA_OK;
+}
+
+ta_status tree_attn_forward(ta_plan_t p, const void* q, const void* k, const void* v, void* o,
+                            float* lse, void* hip_stream) {
+  ta::clear_error();
+  if (p && p->n_q == 0) return TA_OK;
+  const void* ptrs[] = {q, k, v, o};
+  const char* names[] = {"q", "k", "v", "o"};
+  ta_status st = ta::check_tensors(p, ptrs, names, 4, lse);
+  if (st != TA_OK) return st;
+  if (!p->one_shot)
+    return ta::fail(TA_ERR_INVALID_ARGUMENT,
+                    "plan has rows with cached tokens or later chunks; use tree_attn_forward_chunked");
+  hipError_t e = ta::launch_tree_attention(ta::attn_args(p, q, k, v, o, lse), (hipStream_t)hip_stream);
+  if (e != hipSuccess) return ta::hip_fail(e, "tree attention launch");
+  return TA_OK;
+}
+
+ta_status tree_attn_cache_write(ta_plan_t p, const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, int64_t cache_tokens, void* hip_stream) {
+  ta::clear_error();
+  if (p && p->n_q == 0) return TA_OK;
+  const void* ptrs[] = {k_new, v_new, k_cache, v_cache};
+  const char* names[] = {"k_new", "v_new", "k_cache", "v_cache"};
+  ta_status st = ta::check_tensors(p, ptrs, names, 4, nullptr);
+  if (st != TA_OK) return st;
+  if (cache_tokens < p->n_kv)
+    return ta::fail(TA_ERR_WORKSPACE, "cache holds %lld tokens < %lld of the plan's row space",
+                    (long long)cache_tokens, (long long)p->n_kv);
+  const unsigned char* ws = (const unsigned char*)p->d_ws;
+  hipError_t e = ta::launch_cache_write(k_new, v_new, k_cache, v_cache, ws + p->off_rowpos, (int)p->n_q,
+                                        p->cfg.num_kv_heads, p->cfg.head_dim, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return ta::hip_fail(e, "cache write launch");
+  return TA_OK;
+}
+
+ta_status tree_attn_forward_cached(ta_plan_t p, const void* q, const void* k_cache, const void* v_cache,
+                                   int64_t cache_tokens, void* o, float* lse, void* hip_stream) {
+  ta::clear_error();
+  if (p && p->n_q == 0) return TA_OK;
+  const void* ptrs[] = {q, k_cache, v_cache, o};
+  const char* names[] = {"q", "k_cache", "v_cache", "o"};
+  ta_status st = ta::check_tensors(p, ptrs, names, 4, lse);
+  if (st != TA_OK) return st;
+  if (cache_tokens < p->n_kv)
+    return ta::fail(TA_ERR_WORKSPACE, "cache holds %lld tokens < %lld of the plan's row space",
+                    (long long)cache_tokens, (long long)p->n_kv);
+  hipError_t e = ta::launch_tree_attention(ta::attn_args(p, q, k_cache, v_cache, o, lse),
+                                           (hipStream_t)hip_stream);
+  if (e != hipSuccess) return ta::hip_fail(e, "tree attention launch");
+  return TA_OK;
+}
+
+ta_status tree_attn_forward_chunked(ta_plan_t p, const void* q, const void* k_new, const void* v_new,
+                                    void* k_cache, void* v_cache, int64_t cache_tokens, void* o,
+                                    float* lse, void* hip_stream) {
+  ta::clear_error();
+  if (p && p->n_q == 0) return TA_OK;
+  // check everything both launches need before enqueuing the first
+  const void* ptrs[] = {q, k_new, v_new, k_cache, v_cache, o};
+  const char* names[] = {"q", "k_new", "v_new", "k_cache", "v_cache", "o"};
+  ta_status st = ta::check_tensors(p, ptrs, names, 6, lse);
+  if (st != TA_OK) return st;
+  if (cache_tokens < p->n_kv)
+    return ta::fail(TA_ERR_WORKSPACE, "cache holds %lld tokens < %lld of the plan's row space",
+                    (long long)cache_tokens, (long long)p->n_kv);
+  st = tree_attn_cache_write(p, k_new, v_new, k_cache, v_cache, cache_tokens, hip_stream);
+  if (st != TA_OK) return st;
+  return tree_attn_forward_cached(p, q, k_cache, v_cache, cache_tokens, o, lse, hip_stream);
+}
+
+ta_status decision_readout(const float* logits, int32_t n_rows, int32_t ld, const int32_t* row1,
+                           const int32_t* row2, const int32_t* n_letters, const float* T,
+                           int32_t n_dec, float* p_avg, float* p_cal, void* hip_stream) {
+  ta::clear_error();
+  if (n_dec < 0) return ta::fail(TA_ERR_INVALID_ARGUMENT, "n_dec %d < 0", n_dec);
+  if (n_dec == 0) return TA_OK;
+  if (!logits || !row1 || !row2 || !n_letters || !T || !p_avg || !p_cal)
+    return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (ld < 2) return ta::fail(TA_ERR_INVALID_ARGUMENT, "ld %d < 2", ld);
+  if (n_rows < 1) return ta::fail(TA_ERR_INVALID_ARGUMENT, "n_rows %d < 1", n_rows);
+  hipError_t e = ta::launch_decision(logits, n_rows, ld, row1, row2, n_letters, T, n_dec, p_avg, p_cal,
+                                     (hipStream_t)hip_stream);
+  if (e != hipSuccess) return ta::hip_fail(e, "decision launch");
+  return TA_OK;
+}
+
+}  // extern "C"

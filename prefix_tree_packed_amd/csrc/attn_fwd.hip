@@ -1,0 +1,384 @@
+// Tree attention forward for gfx950 (MI355X): block-sparse over the schedule
+// built by the host plan, f16 inputs, MFMA f32 accumulation, f32 online
+// softmax.
+//
+// What it computes: the architecture page "How basal-rs computes a decision",
+// section 03 "Packing" ("Attention over tree blocks": a token attends to the
+// earlier tokens of its own block and to every token of its ancestor blocks)
+// and section 01, stage "GPU forward pass" (one compact f16 token list,
+// attention with f32 accumulation).
+//
+// Work decomposition. One workgroup (4 wave64s) computes one query tile (up to
+// 64 consecutive row tokens) for one KV head and all query heads that share
+// it. The workgroup's columns are (token, head) pairs, head-minor, so the KV
+// tile staged in LDS is reused by group * tokens query rows. Each wave owns
+// 16*NCG columns and keeps its Q fragments in registers for the whole tile.
+//
+// Per 64-key tile (double-buffered in LDS, next tile's global loads issued
+// before the current tile's math):
+//   S^T = K Q^T     v_mfma_f32_16x16x32_f16, A = K rows from LDS, B = Q
+//   mask            only on tiles the plan flags: key u is visible to query t
+//                   iff u's block is a proper ancestor of t's block (Euler
+//                   interval test) or the same block with u <= t
+//   softmax         running max per column (two cross-lane steps over the
+//                   4 lane groups that share a column), exp2 with log2(e)
+//                   folded into the scale, running sum kept per lane
+//   O^T += V^T P^T  A = V^T read from an LDS copy stored transposed, B = P^T
+//                   straight from the S^T accumulators (rounded to f16).
+// Computing the transposed products makes the S^T accumulator layout equal to
+// the B-operand layout the P.V product needs, so P never goes through LDS;
+// the 8 keys a lane holds for one column are {4g..4g+3, 16+4g..16+4g+3} of a
+// 32-key chunk (g = lane / 16), and V^T is read with the same key order.
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+#include "layout.h"
+
+namespace ta {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// Slack (in log2 units) a score may exceed the softmax reference max before
+// the reference is moved and O rescaled.
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D>
+struct AttnLds {
+  static constexpr int KSTR = D + 8;  // halves per K row (16-byte pad)
+  static constexpr int VSTR = 68;     // halves per V^T row: 64 keys + 4
+  _Float16 k[2][kKeyTile * KSTR];
+  _Float16 vt[2][D * VSTR];
+  int2 anc[2][kKeyTile];
+};
+
+template <int D, int G, int NCG, bool OUT_F32>
+__global__ void __launch_bounds__(kAttnThreads)
+tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
+                     const _Float16* __restrict__ V, void* __restrict__ Out,
+                     float* __restrict__ Lse, const QTile* __restrict__ qtiles,
+                     const KTile* __restrict__ ktiles, const int* __restrict__ work,
+                     const int2* __restrict__ tok_anc, int hq, int hkv, int n_q_total,
+                     float scale_log2e) {
+  constexpr int DC = D / 32;                 // 32-wide head-dim chunks (QK^T k-steps)
+  constexpr int DT = D / 16;                 // 16-row head-dim tiles (P.V outputs)
+  constexpr int CPW = 16 * NCG;              // columns per wave
+  constexpr int DCH = D / 8;                 // 16-byte chunks per K/V row
+  constexpr int RPT = kKeyTile * DCH / kAttnThreads;  // K rows / V keys per thread
+  constexpr int KSTR = AttnLds<D>::KSTR;
+  constexpr int VSTR = AttnLds<D>::VSTR;
+  static_assert(RPT == 2 || RPT == 4, "unsupported head_dim");
+
+  __shared__ AttnLds<D> lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+
+  const int wid = work[blockIdx.x];
+  const int qt = wid / hkv;
+  const int kvh = wid - qt * hkv;
+  const QTile tile = qtiles[qt];
+
+  // ---- columns owned by this lane: (token, head) pairs -------------------
+  int tok[NCG], head[NCG], trow[NCG], ttin[NCG];
+  bool cvalid[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const int c = wave * CPW + cg * 16 + l16;
+    int t = c / G;
+    cvalid[cg] = t < tile.n_tok;
+    t = cvalid[cg] ? t : tile.n_tok - 1;  // padded columns mirror the last token
+    tok[cg] = t;
+    head[cg] = kvh * G + (c % G);
+    trow[cg] = tile.q_row + t;
+    ttin[cg] = tok_anc[trow[cg]].x;
+  }
+
+  // ---- Q fragments (B operand of S^T = K Q^T) ------------------------------
+  h8 qf[NCG][DC];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const _Float16* qp =
+        Q + ((size_t)(tile.q_fwd + tok[cg]) * hq + head[cg]) * D + 8 * lg;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) qf[cg][dc] = *(const h8*)(qp + 32 * dc);
+  }
+
+  f4 oacc[DT][NCG];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) oacc[dt][cg] = f4{0.f, 0.f, 0.f, 0.f};
+  float mrun[NCG], lrun[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    mrun[cg] = -1e30f;  // finite: a column whose first tiles are all masked stays NaN-free
+    lrun[cg] = 0.f;
+  }
+
+  // ---- K/V staging -------------------------------------------------------
+  const size_t kv_stride = (size_t)hkv * D;
+  const _Float16* Kh = K + (size_t)kvh * D;
+  const _Float16* Vh = V + (size_t)kvh * D;
+  const int dch = tid % DCH;
+  const int rgrp = tid / DCH;  // K rows rgrp + r*(256/DCH); V keys rgrp*RPT + r
+  h8 kreg[RPT], vreg[RPT];
+  int2 areg = int2{0, 0};
+
+  auto gload = [&](int kt) {
+    const KTile kti = ktiles[kt];
+    const int nk = kti.meta & 0xffff;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int row = rgrp + r * (kAttnThreads / DCH);
+      kreg[r] = row < nk ? *(const h8*)(Kh + (size_t)(kti.k0 + row) * kv_stride + 8 * dch)
+                         : h8{0, 0, 0, 0, 0, 0, 0, 0};
+      const int key = rgrp * RPT + r;
+      vreg[r] = key < nk ? *(const h8*)(Vh + (size_t)(kti.k0 + key) * kv_stride + 8 * dch)
+                         : h8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    if ((kti.meta & kMaskedBit) && tid < kKeyTile)
+      areg = tid < nk ? tok_anc[kti.k0 + tid] : int2{0, 0};
+  };
+
+  auto lstore = [&](int s, int kt) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int row = rgrp + r * (kAttnThreads / DCH);
+      *(h8*)&lds.k[s][row * KSTR + 8 * dch] = kreg[r];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      _Float16* dst = &lds.vt[s][(8 * dch + i) * VSTR + rgrp * RPT];
+      if constexpr (RPT == 4) {
+        *(h4*)dst = h4{vreg[0][i], vreg[1][i], vreg[2][i], vreg[3][i]};
+      } else {
+        *(h2*)dst = h2{vreg[0][i], vreg[1][i]};
+      }
+    }
+    if ((ktiles[kt].meta & kMaskedBit) && tid < kKeyTile) lds.anc[s][tid] = areg;
+  };
+
+  const int ktb = tile.kt_begin, kte = tile.kt_end;
+  if (kte <= ktb) return;  // never planned (a token always sees itself); uniform per workgroup
+  gload(ktb);
+  lstore(0, ktb);
+  __syncthreads();
+
+  for (int kt = ktb; kt < kte; ++kt) {
+    const int s = (kt - ktb) & 1;
+    const KTile cur = ktiles[kt];
+    const bool has_next = kt + 1 < kte;
+    if (has_next) gload(kt + 1);
+
+    const _Float16* kl = &lds.k[s][0];
+    const _Float16* vl = &lds.vt[s][0];
+    const int nk = cur.meta & 0xffff;
+    const bool masked = (cur.meta & kMaskedBit) != 0;
+
+    // The 64-key tile is processed as two 32-key halves (S, softmax, P.V each),
+    // which keeps the S^T and P^T fragments of one half in registers.
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      // ---- S^T = K Q^T for keys [32*half, 32*half + 32) ------------------------
+      f4 sacc[2][NCG];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) sacc[k2][cg] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int ks = 2 * half + k2;
+          const h8 a = *(const h8*)(kl + (16 * ks + l16) * KSTR + 32 * dc + 8 * lg);
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg)
+            sacc[k2][cg] =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[cg][dc], sacc[k2][cg], 0, 0, 0);
+        }
+      }
+
+      // ---- visibility on flagged tiles ------------------------------------------
+      if (masked) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kidx = 32 * half + 16 * k2 + 4 * lg + r;
+            const int2 an = lds.anc[s][kidx];
+            const int u = cur.k0 + kidx;
+#pragma unroll
+            for (int cg = 0; cg < NCG; ++cg) {
+              const bool vis = (kidx < nk) & (((an.x < ttin[cg]) & (ttin[cg] < an.y)) |
+                                              ((an.x == ttin[cg]) & (u <= trow[cg])));
+              sacc[k2][cg][r] = vis ? sacc[k2][cg][r] : -__builtin_inff();
+            }
+          }
+        }
+      }
+
+      // ---- online softmax with a lazily moved reference max ----------------------
+      // P = exp2(S*c - m) with any m >= the running max minus kRescaleSlack gives
+      // the same normalised result; m is only raised (and O, l rescaled) when a
+      // score exceeds it by more than kRescaleSlack, so P stays <= 2^kRescaleSlack.
+      float mnew[NCG];
+      bool need_any = false;
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
+        float mx = sacc[0][cg][0];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[k2][cg][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float ms = mx * scale_log2e;
+        const bool need = ms > mrun[cg] + kRescaleSlack;
+        mnew[cg] = need ? ms : mrun[cg];
+        need_any |= need;
+      }
+      if (__any(need_any)) {
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) {
+          const float alpha = __builtin_amdgcn_exp2f(mrun[cg] - mnew[cg]);
+          mrun[cg] = mnew[cg];
+          lrun[cg] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oacc[dt][cg] *= alpha;
+        }
+      }
+      h8 pb[NCG];
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
+        float lsum = 0.f;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pv =
+                __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[k2][cg][r], scale_log2e, -mrun[cg]));
+            lsum += pv;
+            pb[cg][k2 * 4 + r] = (_Float16)pv;
+          }
+        }
+        lrun[cg] += lsum;
+      }
+
+      // ---- O^T += V^T P^T over the same 32 keys -----------------------------------
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const _Float16* row = vl + (16 * dt + l16) * VSTR + 32 * half + 4 * lg;
+        const h4 lo = *(const h4*)row;
+        const h4 hi = *(const h4*)(row + 16);
+        const h8 a = h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) {
+          oacc[dt][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[cg], oacc[dt][cg], 0, 0, 0);
+          // keep the O accumulators in AGPRs (MFMA reads and writes them there)
+          asm volatile("" : "+a"(oacc[dt][cg]));
+        }
+      }
+    }
+
+    if (has_next) lstore(s ^ 1, kt + 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2 ------------------------
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    float lt = lrun[cg];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = 1.0f / lt;
+    if (!cvalid[cg]) continue;
+    const size_t obase = ((size_t)(tile.q_fwd + tok[cg]) * hq + head[cg]) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const f4 val = oacc[dt][cg] * inv;
+      const int d0 = 16 * dt + 4 * lg;
+      if constexpr (OUT_F32) {
+        *(f4*)((float*)Out + obase + d0) = val;
+      } else {
+        *(h4*)((_Float16*)Out + obase + d0) =
+            h4{(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
+      }
+    }
+    if (Lse != nullptr && lg == 0)
+      Lse[(size_t)head[cg] * n_q_total + tile.q_fwd + tok[cg]] =
+          (mrun[cg] + __log2f(lt)) * 0.69314718055994530942f;
+  }
+}
+
+// Copies this forward's K/V rows into the row-space cache: forward token t
+// goes to cache row tok_rowpos[t]. One thread per 16-byte chunk.
+__global__ void __launch_bounds__(256)
+cache_write_kernel(const _Float16* __restrict__ k_new, const _Float16* __restrict__ v_new,
+                   _Float16* __restrict__ k_cache, _Float16* __restrict__ v_cache,
+                   const int* __restrict__ tok_rowpos, int n_q, int row_chunks) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)n_q * row_chunks;
+  if (i >= total) return;
+  const int t = (int)(i / row_chunks);
+  const int c = (int)(i - (long long)t * row_chunks);
+  const size_t src = (size_t)t * row_chunks + c;
+  const size_t dst = (size_t)tok_rowpos[t] * row_chunks + c;
+  ((h8*)k_cache)[dst] = ((const h8*)k_new)[src];
+  ((h8*)v_cache)[dst] = ((const h8*)v_new)[src];
+}
+
+template <int D, int G, int NCG, bool F32>
+static hipError_t launch_variant(const AttnArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((tree_attn_fwd_kernel<D, G, NCG, F32>), dim3(a.n_work), dim3(kAttnThreads), 0,
+                     st, (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v, a.o,
+                     a.lse, (const QTile*)a.qtiles, (const KTile*)a.ktiles, (const int*)a.work,
+                     (const int2*)a.tok_anc, a.hq, a.hkv, a.n_q, a.scale_log2e);
+  return hipGetLastError();
+}
+
+template <int D, int G>
+static hipError_t launch_group(const AttnArgs& a, hipStream_t st) {
+  constexpr int NCG = column_groups_for(G, D);
+  return a.out_f32 ? launch_variant<D, G, NCG, true>(a, st) : launch_variant<D, G, NCG, false>(a, st);
+}
+
+template <int D>
+static hipError_t launch_dim(const AttnArgs& a, hipStream_t st) {
+  switch (a.group) {
+    case 1: return launch_group<D, 1>(a, st);
+    case 2: return launch_group<D, 2>(a, st);
+    case 4: return launch_group<D, 4>(a, st);
+    case 8: return launch_group<D, 8>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_tree_attention(const AttnArgs& a, hipStream_t st) {
+  if (a.n_work == 0) return hipSuccess;
+  switch (a.head_dim) {
+    case 64: return launch_dim<64>(a, st);
+    case 128: return launch_dim<128>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const void* tok_rowpos, int n_q, int hkv, int head_dim,
+                              hipStream_t st) {
+  if (n_q == 0) return hipSuccess;
+  const int row_chunks = hkv * head_dim / 8;
+  const long long total = (long long)n_q * row_chunks;
+  const int blocks = (int)((total + 255) / 256);
+  hipLaunchKernelGGL(cache_write_kernel, dim3(blocks), dim3(256), 0, st, (const _Float16*)k_new,
+                     (const _Float16*)v_new, (_Float16*)k_cache, (_Float16*)v_cache,
+                     (const int*)tok_rowpos, n_q, row_chunks);
+  return hipGetLastError();
+}
+
+}  // namespace ta

@@ -1,0 +1,53 @@
+// Error reporting and the plan object shared by the host sources of the
+// tree-attention library.
+#pragma once
+
+#include <stdarg.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/tree_attn.h"
+#include "layout.h"
+
+namespace ta {
+
+// Set the thread-local message returned by tree_attn_last_error() and return `st`.
+ta_status fail(ta_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+const char* last_error();
+
+struct Int2 {
+  int32_t x, y;
+};
+
+}  // namespace ta
+
+struct ta_plan_s {
+  ta_attn_cfg cfg;
+  int group = 1;            // query heads per KV head
+  int q_tile_tokens = 64;
+
+  int64_t n_q = 0, n_kv = 0, useful_pairs = 0, cost_packed = 0, cost_separate = 0;
+  int32_t num_rows = 0, num_blocks = 0, max_depth = 0;
+  int one_shot = 1;
+
+  // host tables (export / tests)
+  std::vector<int32_t> pos_id, tok_row, tok_block, tok_offset, leaf_block, leaf_tok;
+
+  // device tables, laid out in `image` at the offsets below (256-byte aligned)
+  std::vector<ta::QTile> qtiles;
+  std::vector<ta::KTile> ktiles;
+  std::vector<int32_t> work;        // qtile * num_kv_heads + kv_head, launch order
+  std::vector<ta::Int2> tok_anc;    // per row-space token: (tin, tout) of its block
+  std::vector<int32_t> tok_rowpos;  // per forward token: its row-space index
+  int64_t n_masked_ktiles = 0;
+
+  size_t off_qtiles = 0, off_ktiles = 0, off_work = 0, off_anc = 0, off_rowpos = 0;
+  size_t ws_bytes = 0;
+  std::vector<unsigned char> image;
+
+  void* d_ws = nullptr;  // workspace of the latest upload
+};

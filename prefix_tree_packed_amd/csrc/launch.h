@@ -1,0 +1,31 @@
+// Host-side launchers of the library's kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace ta {
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const void* qtiles;
+  const void* ktiles;
+  const void* work;
+  const void* tok_anc;
+  int hq, hkv, head_dim, group, n_q, n_work;
+  float scale_log2e;
+  bool out_f32;
+};
+
+hipError_t launch_tree_attention(const AttnArgs& a, hipStream_t st);
+hipError_t launch_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const void* tok_rowpos, int n_q, int hkv, int head_dim,
+                              hipStream_t st);
+hipError_t launch_decision(const float* logits, int n_rows, int ld, const int* row1, const int* row2,
+                           const int* n_letters, const float* T, int n_dec, float* p_avg,
+                           float* p_cal, hipStream_t st);
+
+}  // namespace ta

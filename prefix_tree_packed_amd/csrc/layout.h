@@ -1,0 +1,48 @@
+// Internal layout shared by the host plan builder and the HIP kernels of the
+// tree-attention library. Not part of the public C ABI (include/tree_attn.h).
+#pragma once
+
+#include <stdint.h>
+
+namespace ta {
+
+// Keys per LDS key tile.
+constexpr int kKeyTile = 64;
+// Threads per attention workgroup: four wave64s.
+constexpr int kAttnThreads = 256;
+
+// One query tile: up to q_tile_tokens consecutive tokens of one row (they may
+// span several blocks). Its key tiles are ktiles[kt_begin, kt_end).
+struct QTile {
+  int32_t q_fwd;     // forward index of the first query token
+  int32_t q_row;     // row-space index of the first query token
+  int32_t n_tok;     // tokens in the tile (>= 1)
+  int32_t kt_begin;
+  int32_t kt_end;
+  int32_t pad0, pad1, pad2;
+};
+
+// One key tile: keys [k0, k0 + n) in row space, n <= kKeyTile. `meta` holds n
+// in its low 16 bits and, in bit 16, whether the tile needs the per-element
+// visibility test (some key is not visible to every query of the tile, or the
+// tile is short).
+struct KTile {
+  int32_t k0;
+  int32_t meta;
+};
+
+constexpr int32_t kMaskedBit = 1 << 16;
+
+// Kernel variant for a head group size (query heads per KV head) and head
+// dimension: the number of 16-column MFMA groups each wave owns. Columns of a
+// workgroup are (token, head) pairs, head-minor; 4 waves x 16*ncg columns =
+// tokens * group. At head_dim 128 two groups per wave keep every fragment in
+// registers without spilling.
+inline constexpr int column_groups_for(int group, int head_dim) {
+  return head_dim >= 128 ? (group >= 2 ? 2 : 1) : (group >= 4 ? 4 : group);
+}
+inline constexpr int q_tile_tokens_for(int group, int head_dim) {
+  return 4 * 16 * column_groups_for(group, head_dim) / group;
+}
+
+}  // namespace ta

@@ -1,0 +1,503 @@
+// Host side of the tree-attention library: validation of a batch's prefix
+// trees and the block-sparse schedule the attention kernel runs.
+//
+// Source: the architecture page "How basal-rs computes a decision",
+//   section 01 "Request path", stage "Batch and prefix tree" (rows of trees,
+//     limits of 32,768 tokens per row, 8,192 per forward, depth 8);
+//   section 03 "Packing", "Attention over tree blocks" (the tree becomes one
+//     row of tokens; a token sees the earlier tokens of its own block and its
+//     ancestor blocks; its RoPE position is its place in its own prompt);
+//   section 01, stage "Validation and planning" (cost counts shared prefixes
+//     once).
+//
+// Schedule. Query tokens of a row are cut into tiles of q_tile_tokens
+// consecutive tokens (a tile may span several blocks of the row, which keeps
+// short leaves from wasting matrix-core lanes). For each tile the keys any of
+// its tokens may see -- the full ranges of its blocks' ancestors plus each own
+// block's prefix up to the tile end -- are merged into disjoint row-space
+// ranges and cut into 64-key tiles. A key tile that every query of the tile
+// sees in full is "unmasked": the kernel skips the visibility test there.
+// Tiles are ordered longest-first so that a plain grid launch schedules them
+// as longest-processing-time-first list scheduling, and the KV heads of a tile
+// are interleaved so that consecutive workgroups (which the dispatcher deals
+// round-robin to the 8 XCDs) keep one KV head per XCD when there are 8.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace ta {
+
+static thread_local std::string g_last_error;
+
+ta_status fail(ta_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+const char* last_error() { return g_last_error.c_str(); }
+
+static constexpr int64_t kRowLimit = 32768;    // section 01, "Batch and prefix tree"
+static constexpr int64_t kForwardLimit = 8192;  // same
+static constexpr int kDepthLimit = 8;           // same
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+namespace {
+
+struct RowView {
+  int64_t base;             // row-space start
+  int32_t first_block;      // global index of the row's first block
+  int32_t nb;
+  int32_t len;
+  int32_t qb, qe;
+  int64_t q_off;            // forward index of token qb
+};
+
+struct Builder {
+  const ta_tree_desc* d;
+  ta_plan_s* p;
+  std::vector<RowView> rows;
+  std::vector<int32_t> start;     // row-local start of each block
+  std::vector<int32_t> parent;    // global parent or -1
+  std::vector<int32_t> depth;
+  std::vector<int32_t> anc_len;   // summed lengths of proper ancestors
+  std::vector<int32_t> tin, tout; // Euler interval of each block over the forest
+  std::vector<uint8_t> has_child;
+
+  ta_status validate_and_layout();
+  void number_blocks();
+  void token_tables();
+  ta_status schedule();
+  int32_t block_of(const RowView& r, int32_t i) const;
+  bool chunk_full(const RowView& r, int32_t k0, int32_t k1, int32_t a,
+                  const std::vector<int32_t>& touched) const;
+};
+
+ta_status Builder::validate_and_layout() {
+  const int R = d->num_rows;
+  if (R < 0) return fail(TA_ERR_INVALID_ARGUMENT, "num_rows %d < 0", R);
+  if (R > 0 && (!d->row_block_indptr || !d->block_parent || !d->block_len))
+    return fail(TA_ERR_INVALID_ARGUMENT, "tree description has a NULL array");
+  if (R > 0 && d->row_block_indptr[0] != 0)
+    return fail(TA_ERR_INVALID_TREE, "row_block_indptr[0] = %d, must be 0", d->row_block_indptr[0]);
+  rows.resize(R);
+  int64_t base = 0, q_off = 0;
+  int64_t nb_total = 0;
+  for (int r = 0; r < R; ++r) {
+    const int64_t a = d->row_block_indptr[r], b = d->row_block_indptr[r + 1];
+    if (b <= a) return fail(TA_ERR_INVALID_TREE, "row %d has no blocks", r);
+    nb_total = b;
+  }
+  if (nb_total > (int64_t)1 << 30) return fail(TA_ERR_LIMIT, "too many blocks (%lld)", (long long)nb_total);
+  start.assign(nb_total, 0);
+  parent.assign(nb_total, -1);
+  depth.assign(nb_total, 0);
+  anc_len.assign(nb_total, 0);
+  has_child.assign(nb_total, 0);
+  p->max_depth = 0;
+  for (int r = 0; r < R; ++r) {
+    const int32_t a = d->row_block_indptr[r], b = d->row_block_indptr[r + 1];
+    int64_t cursor = 0;
+    for (int32_t g = a; g < b; ++g) {
+      const int32_t local = g - a;
+      const int32_t len = d->block_len[g];
+      if (len < 1) return fail(TA_ERR_INVALID_TREE, "row %d block %d has length %d < 1", r, local, len);
+      const int32_t pl = d->block_parent[g];
+      if (pl < -1 || pl >= local)
+        return fail(TA_ERR_INVALID_TREE,
+                    "row %d block %d has parent %d; parents must be -1 or an earlier block of the row",
+                    r, local, pl);
+      start[g] = (int32_t)std::min<int64_t>(cursor, INT32_MAX);
+      cursor += len;
+      if (cursor > kRowLimit)
+        return fail(TA_ERR_LIMIT, "row %d holds more than %lld tokens", r, (long long)kRowLimit);
+      if (pl < 0) {
+        parent[g] = -1;
+        depth[g] = 1;
+        anc_len[g] = 0;
+      } else {
+        const int32_t pg = a + pl;
+        parent[g] = pg;
+        depth[g] = depth[pg] + 1;
+        anc_len[g] = anc_len[pg] + d->block_len[pg];
+        has_child[pg] = 1;
+      }
+      if (depth[g] > kDepthLimit)
+        return fail(TA_ERR_LIMIT, "row %d block %d is at depth %d > %d", r, local, depth[g], kDepthLimit);
+      p->max_depth = std::max(p->max_depth, depth[g]);
+    }
+    RowView& v = rows[r];
+    v.base = base;
+    v.first_block = a;
+    v.nb = b - a;
+    v.len = (int32_t)cursor;
+    v.qb = d->row_q_begin ? d->row_q_begin[r] : 0;
+    v.qe = d->row_q_end ? d->row_q_end[r] : v.len;
+    if (v.qb < 0 || v.qb > v.qe || v.qe > v.len)
+      return fail(TA_ERR_INVALID_ARGUMENT, "row %d: query span [%d, %d) not inside [0, %d]", r, v.qb,
+                  v.qe, v.len);
+    v.q_off = q_off;
+    q_off += v.qe - v.qb;
+    base += v.len;
+    if (v.qb != 0 || v.qe != v.len) p->one_shot = 0;
+  }
+  if (q_off > kForwardLimit)
+    return fail(TA_ERR_LIMIT, "forward computes %lld tokens > %lld", (long long)q_off,
+                (long long)kForwardLimit);
+  if (base > (int64_t)INT32_MAX - 2 * kRowLimit)
+    return fail(TA_ERR_LIMIT, "row space of %lld tokens does not fit 32-bit indexing", (long long)base);
+  p->n_q = q_off;
+  p->n_kv = base;
+  p->num_rows = R;
+  p->num_blocks = (int32_t)nb_total;
+  return TA_OK;
+}
+
+// Euler numbering over each row's forest: tin = pre-order index, tout = tin +
+// blocks in the subtree. Block A is a proper ancestor of B iff
+// tin[A] < tin[B] < tout[A]. Numbers are global, so different rows (and
+// different trees of one row) have disjoint intervals.
+void Builder::number_blocks() {
+  const int32_t NB = (int32_t)start.size();
+  tin.assign(NB, 0);
+  tout.assign(NB, 0);
+  std::vector<std::vector<int32_t>> kids(NB);
+  for (int32_t g = 0; g < NB; ++g)
+    if (parent[g] >= 0) kids[parent[g]].push_back(g);
+  int32_t counter = 0;
+  std::vector<std::pair<int32_t, size_t>> stack;
+  for (const RowView& r : rows) {
+    for (int32_t g = r.first_block; g < r.first_block + r.nb; ++g) {
+      if (parent[g] >= 0) continue;
+      stack.push_back({g, 0});
+      tin[g] = counter++;
+      while (!stack.empty()) {
+        auto& top = stack.back();
+        if (top.second < kids[top.first].size()) {
+          const int32_t c = kids[top.first][top.second++];
+          tin[c] = counter++;
+          stack.push_back({c, 0});
+        } else {
+          tout[top.first] = counter;
+          stack.pop_back();
+        }
+      }
+    }
+  }
+}
+
+void Builder::token_tables() {
+  const int64_t nq = p->n_q;
+  p->pos_id.resize(nq);
+  p->tok_row.resize(nq);
+  p->tok_block.resize(nq);
+  p->tok_offset.resize(nq);
+  p->tok_rowpos.resize(nq);
+  p->tok_anc.resize(p->n_kv);
+  p->useful_pairs = 0;
+  p->cost_separate = 0;
+  p->leaf_block.clear();
+  p->leaf_tok.clear();
+  for (int r = 0; r < (int)rows.size(); ++r) {
+    const RowView& v = rows[r];
+    for (int32_t g = v.first_block; g < v.first_block + v.nb; ++g) {
+      const int32_t s = start[g], len = d->block_len[g];
+      for (int32_t i = s; i < s + len; ++i) p->tok_anc[v.base + i] = Int2{tin[g], tout[g]};
+      const int32_t lo = std::max(s, v.qb), hi = std::min(s + len, v.qe);
+      for (int32_t i = lo; i < hi; ++i) {
+        const int64_t t = v.q_off + (i - v.qb);
+        const int32_t pos = anc_len[g] + (i - s);
+        p->pos_id[t] = pos;
+        p->tok_row[t] = r;
+        p->tok_block[t] = g;
+        p->tok_offset[t] = i - s;
+        p->tok_rowpos[t] = (int32_t)(v.base + i);
+        p->useful_pairs += pos + 1;
+      }
+      if (!has_child[g]) {
+        p->cost_separate += anc_len[g] + len;
+        const int32_t last = s + len - 1;
+        if (last >= v.qb && last < v.qe) {
+          p->leaf_block.push_back(g);
+          p->leaf_tok.push_back((int32_t)(v.q_off + last - v.qb));
+        }
+      }
+    }
+  }
+  p->cost_packed = p->n_q;
+}
+
+int32_t Builder::block_of(const RowView& r, int32_t i) const {
+  // blocks of a row start at increasing offsets
+  const int32_t* s = start.data() + r.first_block;
+  const int32_t k = (int32_t)(std::upper_bound(s, s + r.nb, i) - s) - 1;
+  return r.first_block + k;
+}
+
+// Every key in [k0, k1) (row-local) is visible to every query token of the
+// tile starting at row-local token `a` whose blocks are `touched`.
+bool Builder::chunk_full(const RowView& r, int32_t k0, int32_t k1, int32_t a,
+                         const std::vector<int32_t>& touched) const {
+  int32_t x = k0;
+  while (x < k1) {
+    const int32_t A = block_of(r, x);
+    const int32_t y = std::min(k1, start[A] + d->block_len[A]);
+    for (int32_t B : touched) {
+      const bool proper_anc = tin[A] < tin[B] && tin[B] < tout[A];
+      // the first token of B inside the tile is max(a, start[B]); a key of B
+      // itself is seen by all of B's tile tokens iff it is not after that one
+      const bool own_prefix = (A == B) && (y - 1 <= std::max(a, start[B]));
+      if (!proper_anc && !own_prefix) return false;
+    }
+    x = y;
+  }
+  return true;
+}
+
+ta_status Builder::schedule() {
+  const int TQ = p->q_tile_tokens;
+  const int hkv = p->cfg.num_kv_heads;
+  p->qtiles.clear();
+  p->ktiles.clear();
+  p->n_masked_ktiles = 0;
+  std::vector<std::pair<int32_t, int32_t>> ranges;
+  std::vector<int32_t> touched;
+  for (const RowView& v : rows) {
+    for (int32_t a = v.qb; a < v.qe; a += TQ) {
+      const int32_t b = std::min(a + TQ, v.qe);
+      const int32_t B0 = block_of(v, a), B1 = block_of(v, b - 1);
+      touched.clear();
+      ranges.clear();
+      for (int32_t B = B0; B <= B1; ++B) {
+        touched.push_back(B);
+        for (int32_t A = parent[B]; A >= 0; A = parent[A])
+          ranges.push_back({start[A], start[A] + d->block_len[A]});
+        ranges.push_back({start[B], std::min(start[B] + d->block_len[B], b)});
+      }
+      std::sort(ranges.begin(), ranges.end());
+      QTile qt{};
+      qt.q_fwd = (int32_t)(v.q_off + (a - v.qb));
+      qt.q_row = (int32_t)(v.base + a);
+      qt.n_tok = b - a;
+      qt.kt_begin = (int32_t)p->ktiles.size();
+      size_t i = 0;
+      while (i < ranges.size()) {
+        int32_t s = ranges[i].first, e = ranges[i].second;
+        size_t j = i + 1;
+        while (j < ranges.size() && ranges[j].first <= e) {
+          e = std::max(e, ranges[j].second);
+          ++j;
+        }
+        for (int32_t k0 = s; k0 < e; k0 += kKeyTile) {
+          const int32_t k1 = std::min(k0 + kKeyTile, e);
+          const bool full = (k1 - k0 == kKeyTile) && chunk_full(v, k0, k1, a, touched);
+          KTile kt;
+          kt.k0 = (int32_t)(v.base + k0);
+          kt.meta = (k1 - k0) | (full ? 0 : kMaskedBit);
+          p->ktiles.push_back(kt);
+          if (!full) ++p->n_masked_ktiles;
+        }
+        i = j;
+      }
+      qt.kt_end = (int32_t)p->ktiles.size();
+      if ((int64_t)p->ktiles.size() > (int64_t)INT32_MAX / 2)
+        return fail(TA_ERR_LIMIT, "schedule too large");
+      p->qtiles.push_back(qt);
+    }
+  }
+  // longest-first order of query tiles; masked key tiles cost a little more
+  const int32_t nqt = (int32_t)p->qtiles.size();
+  std::vector<double> cost(nqt);
+  for (int32_t t = 0; t < nqt; ++t) {
+    double c = 0;
+    for (int32_t k = p->qtiles[t].kt_begin; k < p->qtiles[t].kt_end; ++k)
+      c += (p->ktiles[k].meta & kMaskedBit) ? 1.25 : 1.0;
+    cost[t] = c;
+  }
+  std::vector<int32_t> order(nqt);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return cost[x] > cost[y]; });
+  p->work.clear();
+  p->work.reserve((size_t)nqt * hkv);
+  for (int32_t t : order)
+    for (int h = 0; h < hkv; ++h) p->work.push_back(t * hkv + h);
+  if ((int64_t)nqt * hkv > (int64_t)INT32_MAX / 2) return fail(TA_ERR_LIMIT, "too many work items");
+  return TA_OK;
+}
+
+}  // namespace
+
+static ta_status check_cfg(const ta_attn_cfg* c) {
+  if (c->num_q_heads < 1 || c->num_kv_heads < 1)
+    return fail(TA_ERR_INVALID_ARGUMENT, "head counts must be >= 1 (got %d, %d)", c->num_q_heads,
+                c->num_kv_heads);
+  if (c->num_q_heads % c->num_kv_heads != 0)
+    return fail(TA_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                c->num_q_heads, c->num_kv_heads);
+  const int g = c->num_q_heads / c->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(TA_ERR_LIMIT, "query heads per KV head = %d; supported: 1, 2, 4, 8", g);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(TA_ERR_LIMIT, "head_dim %d; supported: 64, 128", c->head_dim);
+  if (!(c->scale > 0.0f) || !isfinite(c->scale))
+    return fail(TA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+  if (c->out_dtype != TA_F16 && c->out_dtype != TA_F32)
+    return fail(TA_ERR_INVALID_ARGUMENT, "unknown out_dtype %d", (int)c->out_dtype);
+  return TA_OK;
+}
+
+static void build_image(ta_plan_s* p) {
+  size_t off = 0;
+  p->off_qtiles = off;
+  off = align256(off + p->qtiles.size() * sizeof(QTile));
+  p->off_ktiles = off;
+  off = align256(off + p->ktiles.size() * sizeof(KTile));
+  p->off_work = off;
+  off = align256(off + p->work.size() * sizeof(int32_t));
+  p->off_anc = off;
+  off = align256(off + p->tok_anc.size() * sizeof(Int2));
+  p->off_rowpos = off;
+  off = align256(off + p->tok_rowpos.size() * sizeof(int32_t));
+  p->ws_bytes = std::max<size_t>(off, 256);
+  p->image.assign(p->ws_bytes, 0);
+  auto put = [&](size_t o, const void* src, size_t n) {
+    if (n) memcpy(p->image.data() + o, src, n);
+  };
+  put(p->off_qtiles, p->qtiles.data(), p->qtiles.size() * sizeof(QTile));
+  put(p->off_ktiles, p->ktiles.data(), p->ktiles.size() * sizeof(KTile));
+  put(p->off_work, p->work.data(), p->work.size() * sizeof(int32_t));
+  put(p->off_anc, p->tok_anc.data(), p->tok_anc.size() * sizeof(Int2));
+  put(p->off_rowpos, p->tok_rowpos.data(), p->tok_rowpos.size() * sizeof(int32_t));
+}
+
+ta_status build_plan(const ta_tree_desc* desc, const ta_attn_cfg* cfg, ta_plan_s* p) {
+  ta_status st = check_cfg(cfg);
+  if (st != TA_OK) return st;
+  p->cfg = *cfg;
+  p->group = cfg->num_q_heads / cfg->num_kv_heads;
+  p->q_tile_tokens = q_tile_tokens_for(p->group, cfg->head_dim);
+  Builder b{desc, p, {}, {}, {}, {}, {}, {}, {}, {}};
+  if ((st = b.validate_and_layout()) != TA_OK) return st;
+  b.number_blocks();
+  b.token_tables();
+  if ((st = b.schedule()) != TA_OK) return st;
+  build_image(p);
+  return TA_OK;
+}
+
+}  // namespace ta
+
+extern "C" {
+
+ta_status tree_attn_plan(const ta_tree_desc* desc, const ta_attn_cfg* cfg, ta_plan_t* out) {
+  ta::clear_error();
+  if (!desc || !cfg || !out) return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL argument");
+  *out = nullptr;
+  ta_plan_s* p = new (std::nothrow) ta_plan_s();
+  if (!p) return ta::fail(TA_ERR_INVALID_ARGUMENT, "out of host memory");
+  ta_status st;
+  try {
+    st = ta::build_plan(desc, cfg, p);
+  } catch (const std::bad_alloc&) {
+    st = ta::fail(TA_ERR_INVALID_ARGUMENT, "out of host memory");
+  }
+  if (st != TA_OK) {
+    delete p;
+    return st;
+  }
+  *out = p;
+  return TA_OK;
+}
+
+ta_status tree_attn_plan_info(ta_plan_t p, ta_plan_info* out) {
+  ta::clear_error();
+  if (!p || !out) return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL argument");
+  memset(out, 0, sizeof(*out));
+  out->num_q_tokens = p->n_q;
+  out->num_kv_tokens = p->n_kv;
+  out->useful_pairs = p->useful_pairs;
+  out->cost_packed = p->cost_packed;
+  out->cost_separate = p->cost_separate;
+  out->num_rows = p->num_rows;
+  out->num_blocks = p->num_blocks;
+  out->num_leaves = (int32_t)p->leaf_block.size();
+  out->max_depth = p->max_depth;
+  out->num_q_tiles = (int32_t)p->qtiles.size();
+  out->num_work_items = (int32_t)p->work.size();
+  out->num_key_tiles = (int64_t)p->ktiles.size();
+  out->num_masked_key_tiles = p->n_masked_ktiles;
+  out->q_tile_tokens = p->q_tile_tokens;
+  out->one_shot = p->one_shot;
+  out->workspace_bytes = p->ws_bytes;
+  return TA_OK;
+}
+
+ta_status tree_attn_plan_export(ta_plan_t p, int32_t* pos_id, int32_t* tok_row, int32_t* tok_block,
+                                int32_t* tok_offset, int32_t* leaf_block, int32_t* leaf_readout_tok) {
+  ta::clear_error();
+  if (!p) return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL plan");
+  auto cp = [](int32_t* dst, const std::vector<int32_t>& src) {
+    if (dst && !src.empty()) memcpy(dst, src.data(), src.size() * sizeof(int32_t));
+  };
+  cp(pos_id, p->pos_id);
+  cp(tok_row, p->tok_row);
+  cp(tok_block, p->tok_block);
+  cp(tok_offset, p->tok_offset);
+  cp(leaf_block, p->leaf_block);
+  cp(leaf_readout_tok, p->leaf_tok);
+  return TA_OK;
+}
+
+ta_status tree_attn_plan_schedule(ta_plan_t p, int32_t* q_tiles, int32_t* key_tiles, int32_t* work,
+                                  int32_t* tok_anc) {
+  ta::clear_error();
+  if (!p) return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL plan");
+  if (q_tiles)
+    for (size_t i = 0; i < p->qtiles.size(); ++i) {
+      const ta::QTile& q = p->qtiles[i];
+      int32_t* o = q_tiles + 5 * i;
+      o[0] = q.q_fwd;
+      o[1] = q.q_row;
+      o[2] = q.n_tok;
+      o[3] = q.kt_begin;
+      o[4] = q.kt_end;
+    }
+  if (key_tiles)
+    for (size_t i = 0; i < p->ktiles.size(); ++i) {
+      key_tiles[3 * i] = p->ktiles[i].k0;
+      key_tiles[3 * i + 1] = p->ktiles[i].meta & 0xffff;
+      key_tiles[3 * i + 2] = (p->ktiles[i].meta & ta::kMaskedBit) ? 1 : 0;
+    }
+  if (work && !p->work.empty()) memcpy(work, p->work.data(), p->work.size() * sizeof(int32_t));
+  if (tok_anc)
+    for (size_t i = 0; i < p->tok_anc.size(); ++i) {
+      tok_anc[2 * i] = p->tok_anc[i].x;
+      tok_anc[2 * i + 1] = p->tok_anc[i].y;
+    }
+  return TA_OK;
+}
+
+ta_status tree_attn_plan_destroy(ta_plan_t p) {
+  ta::clear_error();
+  delete p;
+  return TA_OK;
+}
+
+const char* tree_attn_last_error(void) { return ta::last_error(); }
+
+}  // extern "C"

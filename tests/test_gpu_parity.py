@@ -1,0 +1,275 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Attention outputs: max-abs <= 2e-3 and relative L2 <= 1e-3 against the oracle
+(the bar stated for this path); decisions: <= 1e-5; plan tables are bit-exact
+(checked on the CPU in test_plan_cpu.py). Small workloads are compared element
+by element; the full-size workloads, in the launch configuration the bench
+times, on sampled query tokens the oracle computes one by one, plus
+properties that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention as OA
+from oracle import decision as OD
+from oracle import tree as OT
+from workloads import configs as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+RL2 = 1e-3
+
+
+@pytest.fixture(scope="module")
+def P():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import prefix_tree_packed_amd as P
+    P.load_library()
+    return P
+
+
+def _dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return t if dtype is None else t.to(dtype)
+
+
+def run_forwards(P, wl, out_dtype="f16", lse=False, forwards=None):
+    """Run a workload's forwards through the C ABI. Chunked workloads share one
+    row-space cache across forwards (its prefix before the first forward
+    filled from the generator's K/V: the template computed at start-up)."""
+    outs, lses, plans = [], [], []
+    fwds = wl.forwards if forwards is None else forwards
+    cache = None
+    for i, f in enumerate(fwds):
+        plan = P.tree_attn_plan(f.tree, wl.hq, wl.hkv, wl.d, wl.scale, out_dtype=out_dtype,
+                                write_lse=lse)
+        P.tree_attn_plan_upload(plan)
+        nq = plan.info["num_q_tokens"]
+        q = _dev(f.q)
+        o = torch.empty((nq, wl.hq, wl.d), dtype=torch.float32 if out_dtype == "f32" else torch.float16,
+                        device="cuda")
+        l = torch.empty((wl.hq, nq), dtype=torch.float32, device="cuda") if lse else None
+        if plan.info["one_shot"] and not wl.chunked:
+            P.tree_attn_forward(plan, q, _dev(f.k_row), _dev(f.v_row), o, l)
+        else:
+            if cache is None or not wl.notes.get("shared_cache", False):
+                kc, vc = f.cache_before()
+                cache = (_dev(kc), _dev(vc))
+            kn, vn = f.kv_new()
+            P.tree_attn_forward_chunked(plan, q, _dev(kn), _dev(vn), cache[0], cache[1], o, l)
+        torch.cuda.synchronize()
+        outs.append(o.float().cpu().numpy())
+        lses.append(None if l is None else l.cpu().numpy())
+        plans.append(plan)
+    return outs, lses, plans, cache
+
+
+def _compare(got, want, atol=ATOL, rl2=RL2, what="O"):
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - want)
+    rel = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert err.max() <= atol, f"{what}: max-abs {err.max():.3e} > {atol}"
+    assert rel <= rl2, f"{what}: rel-L2 {rel:.3e} > {rl2}"
+    return err.max(), rel
+
+
+# ---------------------------------------------------------------------------
+# small workloads, element by element
+# ---------------------------------------------------------------------------
+
+def _small_cases():
+    return [
+        ("cfg0", lambda s: W.make_config(0, s)),
+        ("doc-questions", lambda s: W.small_doc_questions(s)),
+        ("requests", lambda s: W.small_requests(s)),
+        ("long-row-chunks", lambda s: W.small_long_row(s)),
+        ("random-g8", lambda s: W.small_random(s, hq=16, hkv=2)),
+        ("random-g4-d64", lambda s: W.small_random(s, hq=8, hkv=2, d=64)),
+        ("random-g1", lambda s: W.small_random(s, hq=2, hkv=2, d=128)),
+        ("random-g2", lambda s: W.small_random(s, hq=4, hkv=2, d=64)),
+    ]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("case", range(len(_small_cases())), ids=[c[0] for c in _small_cases()])
+@pytest.mark.parametrize("out_dtype", ["f16", "f32"])
+def test_small_parity(P, case, seed, out_dtype):
+    name, make = _small_cases()[case]
+    wl = make(seed)
+    print(f"[parity] {name} seed={seed} out={out_dtype}", flush=True)
+    outs, lses, _, _ = run_forwards(P, wl, out_dtype=out_dtype, lse=True)
+    for f, o, l in zip(wl.forwards, outs, lses):
+        want, want_lse = OA.tree_attention(f.tree, f.q, f.k_row, f.v_row, wl.scale, return_lse=True)
+        _compare(o, want)
+        _compare(l, want_lse, atol=1e-4, rl2=1e-5, what="LSE")
+
+
+def test_edge_trees(P):
+    """Single-token blocks, a depth-8 chain, a forest in one row, ragged tiles."""
+    rng = np.random.default_rng(5)
+    rows = [
+        [(-1, 1), (0, 1), (1, 1), (2, 1), (3, 1), (4, 1), (5, 1), (6, 1)],        # depth 8, 1-token blocks
+        [(-1, 3), (0, 1), (-1, 5), (2, 1), (2, 70), (-1, 1)],                    # forest
+        [(-1, 65)] + [(0, 1)] * 9 + [(0, 129)],                                  # many siblings
+        [(-1, 100)] + [(i, 7) for i in range(7)],                                # chain over tiles
+    ]
+    desc = W.desc_from_rows(rows)
+    for hq, hkv, d in ((8, 2, 128), (8, 1, 64), (4, 4, 64)):
+        f = W.draw_forward(rng, desc, hq, hkv, d)
+        wl = W.Workload("edge", hq, hkv, d, [f], None)
+        outs, _, _, _ = run_forwards(P, wl, out_dtype="f32")
+        want = OA.tree_attention(desc, f.q, f.k_row, f.v_row, wl.scale)
+        _compare(outs[0], want)
+
+
+def test_empty_forward_and_one_shot_refusal(P):
+    desc = W.desc_from_rows([[(-1, 40), (0, 9)]], [(40, 49)])
+    plan = P.tree_attn_plan(desc, 4, 2, 64, 0.125)
+    P.tree_attn_plan_upload(plan)
+    z = torch.zeros((9, 4, 64), dtype=torch.float16, device="cuda")
+    kv = torch.zeros((9, 2, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(P.TreeAttnError) as ei:
+        P.tree_attn_forward(plan, z, kv, kv, torch.empty_like(z))
+    assert ei.value.status == 1
+    empty = W.desc_from_rows([[(-1, 40)]], [(40, 40)])
+    plan0 = P.tree_attn_plan(empty, 4, 2, 64, 0.125)
+    P.tree_attn_plan_upload(plan0)
+    e = torch.zeros((0, 4, 64), dtype=torch.float16, device="cuda")
+    ekv = torch.zeros((0, 2, 64), dtype=torch.float16, device="cuda")
+    cache = torch.zeros((40, 2, 64), dtype=torch.float16, device="cuda")
+    P.tree_attn_forward_chunked(plan0, e, ekv, ekv, cache, cache.clone(), e.clone())
+    torch.cuda.synchronize()
+
+
+def test_binding_rejects_wrong_shapes(P):
+    desc = W.desc_from_rows([[(-1, 40), (0, 9)]])
+    plan = P.tree_attn_plan(desc, 4, 2, 64, 0.125)
+    P.tree_attn_plan_upload(plan)
+    q = torch.zeros((49, 4, 64), dtype=torch.float16, device="cuda")
+    kv = torch.zeros((48, 2, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        P.tree_attn_forward(plan, q, kv, kv, torch.empty_like(q))
+
+
+def test_deterministic(P):
+    wl = W.small_doc_questions(3)
+    a, _, _, _ = run_forwards(P, wl)
+    b, _, _, _ = run_forwards(P, wl)
+    assert np.array_equal(a[0], b[0])
+
+
+def test_chunked_cache_and_equivalence_with_one_shot(P):
+    """The chunked path writes each chunk's K/V into the cache bit-exactly, and
+    its outputs match a one-shot forward over the complete row."""
+    wl = W.small_long_row(4, doc=500, nq=3, chunk=256)
+    outs, _, _, cache = run_forwards(P, wl, out_dtype="f32")
+    f0 = wl.forwards[0]
+    assert np.array_equal(cache[0].cpu().numpy(), f0.k_row)
+    assert np.array_equal(cache[1].cpu().numpy(), f0.v_row)
+    full = f0.tree.with_q_range([0], [int(f0.tree.row_lengths()[0])])
+    q_all = np.concatenate([f.q for f in wl.forwards])
+    one = W.Workload("one", wl.hq, wl.hkv, wl.d, [W.Forward(full, q_all, f0.k_row, f0.v_row)], None)
+    o1, _, _, _ = run_forwards(P, one, out_dtype="f32")
+    # tiles restart at chunk boundaries, so agreement is up to rounding
+    _compare(np.concatenate(outs), o1[0].astype(np.float64), what="chunked vs one-shot")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: sampled tokens against the oracle
+# ---------------------------------------------------------------------------
+
+def _sample_tokens(desc, rng, n=48):
+    idx = OT.build_index(desc)
+    nq = idx.num_q_tokens
+    _, readout = OT.leaf_readouts(idx)
+    picks = set(rng.integers(0, nq, n).tolist()) | {0, nq - 1}
+    picks |= set(readout[:8].tolist())
+    return np.array(sorted(picks))
+
+
+@pytest.mark.parametrize("cfg,seed", [(1, 0), (2, 0), (3, 0), (4, 0), (4, 1), (4, 2), (4, 3), (4, 4)])
+def test_full_size_sampled(P, cfg, seed):
+    print(f"[full] config {cfg} seed {seed}", flush=True)
+    wl = W.make_config(cfg, seed)
+    outs, lses, plans, _ = run_forwards(P, wl, out_dtype="f16", lse=True)
+    rng = np.random.default_rng(1000 + cfg)
+    for f, o, l, plan in zip(wl.forwards, outs, lses, plans):
+        sel = _sample_tokens(f.tree, rng)
+        want, want_lse = OA.tree_attention(f.tree, f.q, f.k_row, f.v_row, wl.scale, sel=sel,
+                                           return_lse=True)
+        _compare(o[sel], want)
+        _compare(l[:, sel], want_lse, atol=1e-4, rl2=1e-5, what="LSE")
+        # properties over every token: finite, and every output is a convex
+        # combination of visible V rows, so it stays inside the V range
+        assert np.all(np.isfinite(o))
+        vmax = float(np.abs(f.v_row).max())
+        assert np.abs(o).max() <= vmax + 2e-3
+
+
+# ---------------------------------------------------------------------------
+# decision epilogue
+# ---------------------------------------------------------------------------
+
+def _run_decisions(P, logits, row1, row2, nl, T):
+    n_dec, ld = len(row1), logits.shape[1]
+    pa = torch.full((n_dec, ld), -7.0, device="cuda")
+    pc = torch.full((n_dec, ld), -7.0, device="cuda")
+    P.decision_readout(_dev(logits.astype(np.float32)), _dev(np.asarray(row1, np.int32)),
+                       _dev(np.asarray(row2, np.int32)), _dev(np.asarray(nl, np.int32)),
+                       _dev(np.asarray(T, np.float32)), pa, pc)
+    torch.cuda.synchronize()
+    return pa.cpu().numpy(), pc.cpu().numpy()
+
+
+def test_decision_worked_example(P, golden_dir):
+    import json
+    import os
+    g = json.load(open(os.path.join(golden_dir, "decision_worked_example.json")))
+    logits = np.array([g["order1_logits"], g["order2_logits"]], np.float32)
+    pa, pc = _run_decisions(P, logits, [0, 0], [1, 1], [3, 3], [1.0, 0.7])
+    assert [round(float(x), 2) for x in pa[0]] == g["average_2dp"]
+    assert [round(float(x), 2) for x in pc[0]] == g["calibrated_2dp"]
+    wa, wc = OD.decisions(logits, [0, 0], [1, 1], [3, 3], [1.0, 0.7])
+    np.testing.assert_allclose(pa, wa, rtol=0, atol=1e-5)
+    np.testing.assert_allclose(pc, wc, rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("cfg,seed", [(0, 0), (1, 0), (2, 0), (3, 0), (4, 0), (4, 1), (4, 2), (4, 3), (4, 4)])
+def test_decision_configs(P, cfg, seed):
+    dec = W.make_config(cfg, seed).decisions
+    for T_override in (None, 0.7, 1.3):
+        T = dec.T if T_override is None else np.full(dec.n_dec, T_override, np.float32)
+        pa, pc = _run_decisions(P, dec.logits, dec.row1, dec.row2, dec.n_letters, T)
+        wa, wc = OD.decisions(dec.logits, dec.row1, dec.row2, dec.n_letters, T)
+        np.testing.assert_allclose(pa, wa, rtol=0, atol=1e-5)
+        np.testing.assert_allclose(pc, wc, rtol=0, atol=1e-5)
+
+
+def test_decision_wide_clamped_and_invalid(P):
+    rng = np.random.default_rng(9)
+    ld = 255
+    logits = rng.normal(0, 2, (8, ld)).astype(np.float32)
+    logits[6, :] = -30.0
+    logits[6, 0] = 30.0          # order 1: one letter dominates by 60
+    logits[7, :] = -30.0
+    logits[7, ld - 1] = 30.0     # order 2 reversed: same letter
+    row1 = [0, 2, 4, 6, 0, 0, 9, 0]
+    row2 = [1, 3, 5, 7, 1, 1, 1, 1]
+    nl = [255, 2, 77, 255, 1, 3, 3, 3]
+    T = [1.0, 0.5, 2.0, 0.7, 1.0, -1.0, 1.0, float("inf")]
+    pa, pc = _run_decisions(P, logits, row1, row2, nl, T)
+    ok = [0, 1, 2, 3]
+    wa, wc = OD.decisions(logits, [row1[i] for i in ok], [row2[i] for i in ok], [nl[i] for i in ok],
+                          [T[i] for i in ok])
+    np.testing.assert_allclose(pa[ok], wa, rtol=0, atol=1e-5)
+    np.testing.assert_allclose(pc[ok], wc, rtol=0, atol=1e-5)
+    assert pc[3, 1] > 0 and pc[3, 1] < 1e-12  # clamp binds: (1e-12)^(1/T)/Z
+    for i in (4, 5, 6, 7):        # n=1, T<0, row out of range, T=inf
+        assert np.all(np.isnan(pa[i])) and np.all(np.isnan(pc[i]))
+    assert math.isclose(float(pa[1, 2:].sum()), 0.0)

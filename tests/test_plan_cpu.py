@@ -1,0 +1,257 @@
+"""The C-ABI library on the CPU (no GPU calls): exported symbols, the host plan
+bit-exact against the oracle's index tables, the block-sparse schedule
+expanded back to the oracle's dense mask, and every error path that is decided
+before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import tree as OT
+from workloads import configs as W
+
+P = pytest.importorskip("prefix_tree_packed_amd")
+from prefix_tree_packed_amd import binding as B  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libtreeattn.so not built")
+    return B.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    with open(os.path.join(ROOT, "include", "tree_attn.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"^(?:ta_status|const char\*)\s+(\w+)\s*\(", text, re.M))
+    assert {"tree_attn_plan", "tree_attn_forward", "tree_attn_forward_chunked",
+            "decision_readout"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(B.EXPORTED) == declared
+
+
+def _descs():
+    out = [("cfg%d" % i, W.make_config(i, 0, tensors=False)) for i in (0, 1, 2, 3, 4)]
+    out += [("cfg4s%d" % s, W.make_config(4, s, tensors=False)) for s in (1, 2, 3, 4)]
+    out += [("cfg2s1", W.make_config(2, 1, tensors=False))]
+    descs = []
+    for name, wl in out:
+        for j, f in enumerate(wl.forwards):
+            descs.append((f"{name}.f{j}", f.tree, wl.hq, wl.hkv, wl.d))
+    rng = np.random.default_rng(7)
+    for i in range(6):
+        rows = W.random_tree_rows(rng, int(rng.integers(50, 600)), int(rng.integers(1, 5)),
+                                  min_len=1, max_len=90)
+        d = W.desc_from_rows(rows)
+        # some rows start later (cached prefix) and stop early
+        if i % 2:
+            lens = d.row_lengths()
+            qb = [int(rng.integers(0, n)) for n in lens]
+            qe = [int(rng.integers(b, n + 1)) for b, n in zip(qb, lens)]
+            d = d.with_q_range(qb, qe)
+        g = [1, 2, 4, 8][i % 4]
+        descs.append((f"rand{i}", d, 2 * g, 2, [64, 128][i % 2]))
+    # several trees in one row, and single-token blocks
+    descs.append(("forest", W.desc_from_rows([[(-1, 3), (0, 1), (-1, 5), (2, 1), (2, 70), (-1, 1)]]),
+                  8, 2, 128))
+    return descs
+
+
+DESCS = _descs()
+
+
+@pytest.mark.parametrize("k", range(len(DESCS)), ids=[d[0] for d in DESCS])
+def test_plan_tables_bit_exact(lib, k):
+    name, desc, hq, hkv, d = DESCS[k]
+    plan = P.tree_attn_plan(desc, hq, hkv, d, d ** -0.5)
+    info = plan.info
+    ex = P.tree_attn_plan_export(plan)
+    idx = OT.build_index(desc)
+    toks = OT.query_tokens(idx)
+    for key in ("pos_id", "tok_row", "tok_block", "tok_offset"):
+        np.testing.assert_array_equal(ex[key], toks[key], err_msg=key)
+    lb, lt = OT.leaf_readouts(idx)
+    np.testing.assert_array_equal(ex["leaf_block"], lb)
+    np.testing.assert_array_equal(ex["leaf_readout_tok"], lt)
+    packed, separate = OT.costs(idx)
+    assert info["cost_packed"] == packed and info["cost_separate"] == separate
+    assert info["num_q_tokens"] == idx.num_q_tokens
+    assert info["num_kv_tokens"] == idx.num_kv_tokens
+    assert info["useful_pairs"] == int((toks["pos_id"].astype(np.int64) + 1).sum())
+    assert info["max_depth"] == max(idx.block_depth)
+    assert info["num_leaves"] == len(lb)
+    one_shot = all(b == 0 and e == n for b, e, n in zip(idx.row_q_begin, idx.row_q_end, idx.row_len))
+    assert info["one_shot"] == int(one_shot)
+
+
+def _expand_schedule(plan, idx, toks):
+    """Apply the kernel's rule to the exported schedule: a tile's query tokens
+    see all keys of its unmasked key tiles, and the keys of masked tiles that
+    pass the Euler-interval test. Returns the coverage count per (t, u)."""
+    sch = P.tree_attn_plan_schedule(plan)
+    nq, nkv = idx.num_q_tokens, idx.num_kv_tokens
+    cover = np.zeros((nq, nkv), np.int16)
+    tin, tout = sch["tok_anc"][:, 0], sch["tok_anc"][:, 1]
+    seen_q = np.zeros(nq, np.int32)
+    for qf, qr, n, kb, ke in sch["q_tiles"]:
+        seen_q[qf:qf + n] += 1
+        trows = np.arange(qr, qr + n)
+        for k0, nk, masked in sch["key_tiles"][kb:ke]:
+            keys = np.arange(k0, k0 + nk)
+            if masked:
+                vis = ((tin[keys][None, :] < tin[trows][:, None]) &
+                       (tin[trows][:, None] < tout[keys][None, :])) | \
+                      ((tin[keys][None, :] == tin[trows][:, None]) &
+                       (keys[None, :] <= trows[:, None]))
+            else:
+                vis = np.ones((n, nk), bool)
+            cover[qf:qf + n, k0:k0 + nk] += vis
+    assert np.all(seen_q == 1), "every query token in exactly one tile"
+    return sch, cover
+
+
+@pytest.mark.parametrize("k", range(len(DESCS)), ids=[d[0] for d in DESCS])
+def test_schedule_covers_mask_exactly_once(lib, k):
+    name, desc, hq, hkv, d = DESCS[k]
+    idx = OT.build_index(desc)
+    if idx.num_q_tokens * idx.num_kv_tokens > 8192 * 9000:
+        pytest.skip("mask too large for this check")  # the long-row chunks
+    plan = P.tree_attn_plan(desc, hq, hkv, d, d ** -0.5)
+    toks = OT.query_tokens(idx)
+    sch, cover = _expand_schedule(plan, idx, toks)
+    mask = OT.dense_mask(idx, toks)
+    np.testing.assert_array_equal(cover, mask.astype(np.int16))
+    # unmasked tiles must be full 64-key tiles; tiles never exceed 64 keys
+    kt = sch["key_tiles"]
+    assert np.all(kt[:, 1] >= 1) and np.all(kt[:, 1] <= 64)
+    assert np.all(kt[kt[:, 2] == 0, 1] == 64)
+    # the launch order lists every (tile, kv head) once, longest tile first
+    w = sch["work"]
+    assert sorted(w.tolist()) == list(range(len(sch["q_tiles"]) * hkv))
+    assert all(w[i] // hkv == w[i - i % hkv] // hkv for i in range(len(w)))  # heads interleaved
+    costs = []
+    for x in w[::hkv]:
+        kb, ke = sch["q_tiles"][x // hkv][3:5]
+        costs.append(float((1.0 + 0.25 * kt[kb:ke, 2]).sum()))  # masked tiles weigh 1.25
+    assert costs == sorted(costs, reverse=True)
+
+
+def test_long_row_chunks_schedule_rows(lib):
+    """For the 32k-token row's chunks check coverage on sampled query tokens."""
+    wl = W.make_config(3, 0, tensors=False)
+    rng = np.random.default_rng(0)
+    for f in wl.forwards:
+        desc = f.tree
+        idx = OT.build_index(desc)
+        toks = OT.query_tokens(idx)
+        plan = P.tree_attn_plan(desc, wl.hq, wl.hkv, wl.d, wl.d ** -0.5)
+        sch = P.tree_attn_plan_schedule(plan)
+        tin, tout = sch["tok_anc"][:, 0], sch["tok_anc"][:, 1]
+        picks = set(rng.integers(0, idx.num_q_tokens, 24).tolist())
+        for qf, qr, n, kb, ke in sch["q_tiles"]:
+            for t in range(qf, qf + n):
+                if t not in picks:
+                    continue
+                tr = qr + (t - qf)
+                row = np.zeros(idx.num_kv_tokens, np.int16)
+                for k0, nk, masked in sch["key_tiles"][kb:ke]:
+                    keys = np.arange(k0, k0 + nk)
+                    if masked:
+                        vis = ((tin[keys] < tin[tr]) & (tin[tr] < tout[keys])) | \
+                              ((tin[keys] == tin[tr]) & (keys <= tr))
+                    else:
+                        vis = np.ones(nk, bool)
+                    row[k0:k0 + nk] += vis
+                want = OT.dense_mask(idx, toks, [t])[0]
+                np.testing.assert_array_equal(row, want.astype(np.int16))
+
+
+# ---------------------------------------------------------------------------
+# error paths (decided on the host before any launch)
+# ---------------------------------------------------------------------------
+
+def _err(fn, *a, **kw):
+    with pytest.raises(B.TreeAttnError) as ei:
+        fn(*a, **kw)
+    return ei.value.status
+
+
+def test_limits_and_invalid_trees(lib):
+    ok = W.desc_from_rows([[(-1, 4), (0, 4)]])
+    assert P.tree_attn_plan(ok, 4, 1, 64, 0.1).info["num_q_tokens"] == 8
+    chain9 = W.desc_from_rows([[(-1, 2)] + [(i, 2) for i in range(8)]])
+    assert _err(P.tree_attn_plan, chain9, 4, 1, 64, 0.1) == 3
+    chain8 = W.desc_from_rows([[(-1, 2)] + [(i, 2) for i in range(7)]])
+    assert P.tree_attn_plan(chain8, 4, 1, 64, 0.1).info["max_depth"] == 8
+    row = W.desc_from_rows([[(-1, 32769)]], [(32769 - 8, 32769)])
+    assert _err(P.tree_attn_plan, row, 4, 1, 64, 0.1) == 3
+    row_ok = W.desc_from_rows([[(-1, 32768)]], [(32768 - 8192, 32768)])
+    assert P.tree_attn_plan(row_ok, 4, 1, 64, 0.1).info["num_q_tokens"] == 8192
+    fwd = W.desc_from_rows([[(-1, 8193)]])
+    assert _err(P.tree_attn_plan, fwd, 4, 1, 64, 0.1) == 3
+    two_rows = W.desc_from_rows([[(-1, 4096)], [(-1, 4097)]])
+    assert _err(P.tree_attn_plan, two_rows, 4, 1, 64, 0.1) == 3
+    bad_parent = W.desc_from_rows([[(-1, 4), (1, 4)]])
+    assert _err(P.tree_attn_plan, bad_parent, 4, 1, 64, 0.1) == 2
+    bad_parent2 = W.desc_from_rows([[(-1, 4), (-2, 4)]])
+    assert _err(P.tree_attn_plan, bad_parent2, 4, 1, 64, 0.1) == 2
+    zero_len = W.desc_from_rows([[(-1, 4), (0, 0)]])
+    assert _err(P.tree_attn_plan, zero_len, 4, 1, 64, 0.1) == 2
+    empty_row = W.TreeDesc(np.array([0, 1, 1], np.int32), np.array([-1], np.int32),
+                           np.array([3], np.int32), np.array([0, 0], np.int32),
+                           np.array([3, 0], np.int32))
+    assert _err(P.tree_attn_plan, empty_row, 4, 1, 64, 0.1) == 2
+    bad_span = ok.with_q_range([5], [3])
+    assert _err(P.tree_attn_plan, bad_span, 4, 1, 64, 0.1) == 1
+    bad_span2 = ok.with_q_range([0], [9])
+    assert _err(P.tree_attn_plan, bad_span2, 4, 1, 64, 0.1) == 1
+
+
+def test_head_config_errors(lib):
+    ok = W.desc_from_rows([[(-1, 4)]])
+    assert _err(P.tree_attn_plan, ok, 6, 4, 64, 0.1) == 1      # not a multiple
+    assert _err(P.tree_attn_plan, ok, 48, 3, 64, 0.1) == 3     # 16 heads per KV head
+    assert _err(P.tree_attn_plan, ok, 3, 1, 64, 0.1) == 3      # 3 heads per KV head
+    assert _err(P.tree_attn_plan, ok, 4, 1, 96, 0.1) == 3      # head_dim
+    assert _err(P.tree_attn_plan, ok, 4, 1, 64, 0.0) == 1      # scale
+    assert _err(P.tree_attn_plan, ok, 4, 1, 64, float("nan")) == 1
+    assert _err(P.tree_attn_plan, ok, 0, 1, 64, 0.1) == 1
+
+
+def test_forward_needs_upload_and_checks_pointers(lib):
+    """Argument errors return before anything touches a device."""
+    desc = W.desc_from_rows([[(-1, 40), (0, 9)]])
+    plan = P.tree_attn_plan(desc, 4, 2, 64, 0.125)
+    fake = ctypes.c_void_p(4096)
+    st = lib.tree_attn_forward(plan.handle, fake, fake, fake, fake, None, None)
+    assert st == 5  # not uploaded
+    st = lib.tree_attn_forward_chunked(plan.handle, fake, fake, fake, fake, fake, 49, fake, None, None)
+    assert st == 5
+    assert lib.tree_attn_plan_upload(plan.handle, None, 1 << 20, None) == 1
+    assert lib.tree_attn_plan_upload(plan.handle, ctypes.c_void_p(4096), 16, None) == 5
+    assert lib.tree_attn_plan_upload(plan.handle, ctypes.c_void_p(4096 + 8), 1 << 20, None) == 5
+    assert "aligned" in P.tree_attn_last_error()
+    assert lib.decision_readout(fake, 4, 1, fake, fake, fake, fake, 2, fake, fake, None) == 1
+    assert lib.decision_readout(None, 4, 4, fake, fake, fake, fake, 2, fake, fake, None) == 1
+    assert lib.decision_readout(fake, 0, 4, fake, fake, fake, fake, 2, fake, fake, None) == 1
+    assert lib.decision_readout(fake, 4, 4, fake, fake, fake, fake, -1, fake, fake, None) == 1
+    assert lib.decision_readout(None, 0, 0, None, None, None, None, 0, None, None, None) == 0
+
+
+def test_empty_forward(lib):
+    desc = W.desc_from_rows([[(-1, 40)]], [(40, 40)])
+    plan = P.tree_attn_plan(desc, 4, 2, 64, 0.125)
+    assert plan.info["num_q_tokens"] == 0 and plan.info["num_work_items"] == 0
+    # nothing to compute: returns OK without touching the (null) buffers
+    assert lib.tree_attn_forward_chunked(plan.handle, None, None, None, None, None, 0, None, None,
+                                         None) == 0
+    empty = W.TreeDesc(np.array([0], np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32),
+                       np.zeros(0, np.int32), np.zeros(0, np.int32))
+    plan0 = P.tree_attn_plan(empty, 4, 2, 64, 0.125)
+    assert plan0.info["num_q_tokens"] == 0 and plan0.info["num_kv_tokens"] == 0

@@ -301,7 +301,7 @@ def _config3(seed: int, doc: int = 16384, nq: int = 96, qlen: int = 64, leaf: in
                             None if q_all is None else q_all[a:b], k, v))
     dec = _paired_decisions(rng, nq, 4)
     return Workload(CONFIG_NAMES[3], hq, hkv, d, fwds, dec, chunked=True,
-                    notes={"row_tokens": row_len})
+                    notes={"row_tokens": row_len, "shared_cache": True})
 
 
 def random_tree_rows(rng: np.random.Generator, total: int, n_rows: int,
