@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run one plain 256 MiB device copy (known bytes) so "
+                         "profiler byte counters can be scaled against it")
     return ap.parse_args()
 
 
@@ -180,6 +183,14 @@ def main():
     for x in fw:
         assert torch.isfinite(x["o"].float()).all().item(), "non-finite attention output"
 
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, infos, args.cpu_seconds)
     print(json.dumps(out), flush=True)

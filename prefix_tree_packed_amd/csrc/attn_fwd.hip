@@ -45,6 +45,10 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 // the reference is moved and O rescaled.
 constexpr float kRescaleSlack = 8.0f;
 
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return fmaxf(a, fmaxf(b, c));
+}
+
 template <int D>
 struct AttnLds {
   static constexpr int KSTR = D + 8;  // halves per K row (16-byte pad)
@@ -54,8 +58,8 @@ struct AttnLds {
   int2 anc[2][kKeyTile];
 };
 
-template <int D, int G, int NCG, bool OUT_F32>
-__global__ void __launch_bounds__(kAttnThreads)
+template <int D, int G, int NCG, int WAVES, bool OUT_F32>
+__global__ void __launch_bounds__(WAVES * 64)
 tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                      const _Float16* __restrict__ V, void* __restrict__ Out,
                      float* __restrict__ Lse, const QTile* __restrict__ qtiles,
@@ -66,7 +70,8 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   constexpr int DT = D / 16;                 // 16-row head-dim tiles (P.V outputs)
   constexpr int CPW = 16 * NCG;              // columns per wave
   constexpr int DCH = D / 8;                 // 16-byte chunks per K/V row
-  constexpr int RPT = kKeyTile * DCH / kAttnThreads;  // K rows / V keys per thread
+  constexpr int NT = WAVES * 64;             // threads
+  constexpr int RPT = kKeyTile * DCH / NT;   // K rows / V keys per thread
   constexpr int KSTR = AttnLds<D>::KSTR;
   constexpr int VSTR = AttnLds<D>::VSTR;
   static_assert(RPT == 2 || RPT == 4, "unsupported head_dim");
@@ -114,33 +119,60 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) oacc[dt][cg] = f4{0.f, 0.f, 0.f, 0.f};
-  float mrun[NCG], lrun[NCG];
+  float mrun[NCG];
+  f4 lacc[NCG];  // row sums of P, accumulated by MFMA (every component holds the sum)
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
     mrun[cg] = -1e30f;  // finite: a column whose first tiles are all masked stays NaN-free
-    lrun[cg] = 0.f;
+    lacc[cg] = f4{0.f, 0.f, 0.f, 0.f};
   }
+  const _Float16 one = (_Float16)1.0f;
+  const h8 ones = h8{one, one, one, one, one, one, one, one};
 
   // ---- K/V staging -------------------------------------------------------
+  // K: thread loads rows krow0 + 16*r (r < RPT) at 16-byte chunk kch, so the
+  //    16 lanes of a row read it contiguously and write it contiguously.
+  // V: thread loads keys vkey0 .. vkey0+RPT-1 at 16-byte chunk vch and stores
+  //    them transposed; consecutive lanes take consecutive key groups, so a
+  //    transposed row segment is written by consecutive lanes (no bank
+  //    conflicts on the V^T stores).
   const size_t kv_stride = (size_t)hkv * D;
   const _Float16* Kh = K + (size_t)kvh * D;
   const _Float16* Vh = V + (size_t)kvh * D;
-  const int dch = tid % DCH;
-  const int rgrp = tid / DCH;  // K rows rgrp + r*(256/DCH); V keys rgrp*RPT + r
+  constexpr int VGRP = kKeyTile / RPT;  // key groups per 16-byte column of V
+  const int kch = tid % DCH;
+  const int krow0 = tid / DCH;
+  const int vgrp = tid % VGRP;
+  const int vch = tid / VGRP;
+  const int vkey0 = vgrp * RPT;
+  // loop-invariant parts of the per-lane global offsets (elements)
+  int kofs[RPT], vofs[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    kofs[r] = (krow0 + r * (NT / DCH)) * (int)kv_stride + 8 * kch;
+    vofs[r] = (vkey0 + r) * (int)kv_stride + 8 * vch;
+  }
   h8 kreg[RPT], vreg[RPT];
   int2 areg = int2{0, 0};
 
   auto gload = [&](int kt) {
     const KTile kti = ktiles[kt];
     const int nk = kti.meta & 0xffff;
+    const _Float16* kb = Kh + (size_t)kti.k0 * kv_stride;  // wave-uniform
+    const _Float16* vb = Vh + (size_t)kti.k0 * kv_stride;
+    if (nk == kKeyTile) {
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      const int row = rgrp + r * (kAttnThreads / DCH);
-      kreg[r] = row < nk ? *(const h8*)(Kh + (size_t)(kti.k0 + row) * kv_stride + 8 * dch)
-                         : h8{0, 0, 0, 0, 0, 0, 0, 0};
-      const int key = rgrp * RPT + r;
-      vreg[r] = key < nk ? *(const h8*)(Vh + (size_t)(kti.k0 + key) * kv_stride + 8 * dch)
-                         : h8{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int r = 0; r < RPT; ++r) {
+        kreg[r] = *(const h8*)(kb + kofs[r]);
+        vreg[r] = *(const h8*)(vb + vofs[r]);
+      }
+    } else {
+      const h8 z = h8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        kreg[r] = krow0 + r * (NT / DCH) < nk ? *(const h8*)(kb + kofs[r]) : z;
+        vreg[r] = vkey0 + r < nk ? *(const h8*)(vb + vofs[r]) : z;
+      }
     }
     if ((kti.meta & kMaskedBit) && tid < kKeyTile)
       areg = tid < nk ? tok_anc[kti.k0 + tid] : int2{0, 0};
@@ -149,12 +181,12 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   auto lstore = [&](int s, int kt) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      const int row = rgrp + r * (kAttnThreads / DCH);
-      *(h8*)&lds.k[s][row * KSTR + 8 * dch] = kreg[r];
+      const int row = krow0 + r * (NT / DCH);
+      *(h8*)&lds.k[s][row * KSTR + 8 * kch] = kreg[r];
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      _Float16* dst = &lds.vt[s][(8 * dch + i) * VSTR + rgrp * RPT];
+      _Float16* dst = &lds.vt[s][(8 * vch + i) * VSTR + vkey0];
       if constexpr (RPT == 4) {
         *(h4*)dst = h4{vreg[0][i], vreg[1][i], vreg[2][i], vreg[3][i]};
       } else {
@@ -231,11 +263,8 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
       bool need_any = false;
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
-        float mx = sacc[0][cg][0];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[k2][cg][r]);
+        const f4 x = sacc[0][cg], y = sacc[1][cg];
+        float mx = max3f(max3f(x[0], x[1], x[2]), max3f(x[3], y[0], y[1]), fmaxf(y[2], y[3]));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float ms = mx * scale_log2e;
@@ -248,7 +277,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
         for (int cg = 0; cg < NCG; ++cg) {
           const float alpha = __builtin_amdgcn_exp2f(mrun[cg] - mnew[cg]);
           mrun[cg] = mnew[cg];
-          lrun[cg] *= alpha;
+          lacc[cg] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) oacc[dt][cg] *= alpha;
         }
@@ -256,21 +285,23 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
       h8 pb[NCG];
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
-        float lsum = 0.f;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float pv =
                 __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[k2][cg][r], scale_log2e, -mrun[cg]));
-            lsum += pv;
             pb[cg][k2 * 4 + r] = (_Float16)pv;
           }
         }
-        lrun[cg] += lsum;
       }
 
-      // ---- O^T += V^T P^T over the same 32 keys -----------------------------------
+      // ---- O^T += V^T P^T over the same 32 keys; the row sums of P (as
+      // rounded to f16, the same P the product uses) come from one more MFMA
+      // against an all-ones A operand ----------------------------------------------
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg)
+        lacc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[cg], lacc[cg], 0, 0, 0);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const _Float16* row = vl + (16 * dt + l16) * VSTR + 32 * half + 4 * lg;
@@ -278,11 +309,8 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
         const h4 hi = *(const h4*)(row + 16);
         const h8 a = h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-        for (int cg = 0; cg < NCG; ++cg) {
+        for (int cg = 0; cg < NCG; ++cg)
           oacc[dt][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[cg], oacc[dt][cg], 0, 0, 0);
-          // keep the O accumulators in AGPRs (MFMA reads and writes them there)
-          asm volatile("" : "+a"(oacc[dt][cg]));
-        }
       }
     }
 
@@ -293,9 +321,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2 ------------------------
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
-    float lt = lrun[cg];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = lacc[cg][0];
     const float inv = 1.0f / lt;
     if (!cvalid[cg]) continue;
     const size_t obase = ((size_t)(tile.q_fwd + tok[cg]) * hq + head[cg]) * D;
@@ -333,9 +359,9 @@ cache_write_kernel(const _Float16* __restrict__ k_new, const _Float16* __restric
   ((h8*)v_cache)[dst] = ((const h8*)v_new)[src];
 }
 
-template <int D, int G, int NCG, bool F32>
+template <int D, int G, int NCG, int WAVES, bool F32>
 static hipError_t launch_variant(const AttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((tree_attn_fwd_kernel<D, G, NCG, F32>), dim3(a.n_work), dim3(kAttnThreads), 0,
+  hipLaunchKernelGGL((tree_attn_fwd_kernel<D, G, NCG, WAVES, F32>), dim3(a.n_work), dim3(WAVES * 64), 0,
                      st, (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v, a.o,
                      a.lse, (const QTile*)a.qtiles, (const KTile*)a.ktiles, (const int*)a.work,
                      (const int2*)a.tok_anc, a.hq, a.hkv, a.n_q, a.scale_log2e);
@@ -345,7 +371,9 @@ static hipError_t launch_variant(const AttnArgs& a, hipStream_t st) {
 template <int D, int G>
 static hipError_t launch_group(const AttnArgs& a, hipStream_t st) {
   constexpr int NCG = column_groups_for(G, D);
-  return a.out_f32 ? launch_variant<D, G, NCG, true>(a, st) : launch_variant<D, G, NCG, false>(a, st);
+  constexpr int WAVES = waves_for(G, D);
+  return a.out_f32 ? launch_variant<D, G, NCG, WAVES, true>(a, st)
+                   : launch_variant<D, G, NCG, WAVES, false>(a, st);
 }
 
 template <int D>

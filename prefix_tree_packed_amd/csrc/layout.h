@@ -8,8 +8,6 @@ namespace ta {
 
 // Keys per LDS key tile.
 constexpr int kKeyTile = 64;
-// Threads per attention workgroup: four wave64s.
-constexpr int kAttnThreads = 256;
 
 // One query tile: up to q_tile_tokens consecutive tokens of one row (they may
 // span several blocks). Its key tiles are ktiles[kt_begin, kt_end).
@@ -34,15 +32,26 @@ struct KTile {
 constexpr int32_t kMaskedBit = 1 << 16;
 
 // Kernel variant for a head group size (query heads per KV head) and head
-// dimension: the number of 16-column MFMA groups each wave owns. Columns of a
-// workgroup are (token, head) pairs, head-minor; 4 waves x 16*ncg columns =
-// tokens * group. At head_dim 128 two groups per wave keep every fragment in
-// registers without spilling.
+// dimension: waves per workgroup and 16-column MFMA groups per wave. Columns of
+// a workgroup are (token, head) pairs, head-minor: waves x 16*ncg columns =
+// tokens * group. At head_dim 128 a wave owning 2 groups needs about 200
+// registers, so two waves share each SIMD and hide each other's latencies;
+// 8 such waves keep 256 columns per workgroup reading each K/V tile once.
+#ifndef TA_D128_WAVES
+#define TA_D128_WAVES 8
+#endif
+#ifndef TA_D128_NCG
+#define TA_D128_NCG 2
+#endif
+inline constexpr int waves_for(int group, int head_dim) {
+  return (head_dim >= 128 && group >= 4) ? TA_D128_WAVES : 4;
+}
 inline constexpr int column_groups_for(int group, int head_dim) {
-  return head_dim >= 128 ? (group >= 2 ? 2 : 1) : (group >= 4 ? 4 : group);
+  return head_dim >= 128 ? (group >= 4 ? TA_D128_NCG : (group >= 2 ? 2 : 1))
+                         : (group >= 4 ? 4 : group);
 }
 inline constexpr int q_tile_tokens_for(int group, int head_dim) {
-  return 4 * 16 * column_groups_for(group, head_dim) / group;
+  return waves_for(group, head_dim) * 16 * column_groups_for(group, head_dim) / group;
 }
 
 }  // namespace ta
