@@ -155,30 +155,26 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   h8 kreg[RPT], vreg[RPT];
   int2 areg = int2{0, 0};
 
-  auto gload = [&](int kt) {
-    const KTile kti = ktiles[kt];
-    const int nk = kti.meta & 0xffff;
-    const _Float16* kb = Kh + (size_t)kti.k0 * kv_stride;  // wave-uniform
-    const _Float16* vb = Vh + (size_t)kti.k0 * kv_stride;
-    if (nk == kKeyTile) {
+  // Issue the global loads of key tile `t` into registers. Rows past the tile's
+  // key count read the tile's first row instead: such rows only occur in tiles
+  // flagged for the visibility test, which gives their scores -inf, so their
+  // K never matters and their V is multiplied by an exact 0 (it is finite).
+  // Straight-line loads keep all of them in flight together.
+  auto gload = [&](const KTile& t) {
+    const int nk = t.meta & 0xffff;
+    const _Float16* kb = Kh + (size_t)t.k0 * kv_stride;  // wave-uniform
+    const _Float16* vb = Vh + (size_t)t.k0 * kv_stride;
 #pragma unroll
-      for (int r = 0; r < RPT; ++r) {
-        kreg[r] = *(const h8*)(kb + kofs[r]);
-        vreg[r] = *(const h8*)(vb + vofs[r]);
-      }
-    } else {
-      const h8 z = h8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int r = 0; r < RPT; ++r) {
-        kreg[r] = krow0 + r * (NT / DCH) < nk ? *(const h8*)(kb + kofs[r]) : z;
-        vreg[r] = vkey0 + r < nk ? *(const h8*)(vb + vofs[r]) : z;
-      }
+    for (int r = 0; r < RPT; ++r) {
+      const bool kin = krow0 + r * (NT / DCH) < nk;
+      const bool vin = vkey0 + r < nk;
+      kreg[r] = *(const h8*)(kb + (kin ? kofs[r] : 8 * kch));
+      vreg[r] = *(const h8*)(vb + (vin ? vofs[r] : 8 * vch));
     }
-    if ((kti.meta & kMaskedBit) && tid < kKeyTile)
-      areg = tid < nk ? tok_anc[kti.k0 + tid] : int2{0, 0};
+    if ((t.meta & kMaskedBit) && tid < kKeyTile) areg = tok_anc[t.k0 + (tid < nk ? tid : 0)];
   };
 
-  auto lstore = [&](int s, int kt) {
+  auto lstore = [&](int s, const KTile& t) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
       const int row = krow0 + r * (NT / DCH);
@@ -193,95 +189,105 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
         *(h2*)dst = h2{vreg[0][i], vreg[1][i]};
       }
     }
-    if ((ktiles[kt].meta & kMaskedBit) && tid < kKeyTile) lds.anc[s][tid] = areg;
+    if ((t.meta & kMaskedBit) && tid < kKeyTile) lds.anc[s][tid] = areg;
   };
 
   const int ktb = tile.kt_begin, kte = tile.kt_end;
   if (kte <= ktb) return;  // never planned (a token always sees itself); uniform per workgroup
-  gload(ktb);
-  lstore(0, ktb);
+  KTile nxt = ktiles[ktb];
+  gload(nxt);
+  lstore(0, nxt);
   __syncthreads();
 
   for (int kt = ktb; kt < kte; ++kt) {
     const int s = (kt - ktb) & 1;
-    const KTile cur = ktiles[kt];
+    const KTile cur = nxt;
     const bool has_next = kt + 1 < kte;
-    if (has_next) gload(kt + 1);
+    if (has_next) {
+      nxt = ktiles[kt + 1];
+      gload(nxt);
+    }
 
     const _Float16* kl = &lds.k[s][0];
     const _Float16* vl = &lds.vt[s][0];
     const int nk = cur.meta & 0xffff;
     const bool masked = (cur.meta & kMaskedBit) != 0;
 
-    // The 64-key tile is processed as two 32-key halves (S, softmax, P.V each),
-    // which keeps the S^T and P^T fragments of one half in registers.
-#pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
-      // ---- S^T = K Q^T for keys [32*half, 32*half + 32) ------------------------
-      f4 sacc[2][NCG];
+    // ---- S^T = K Q^T for the whole 64-key tile --------------------------------
+    f4 sacc[4][NCG];
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int cg = 0; cg < NCG; ++cg) sacc[k2][cg] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int cg = 0; cg < NCG; ++cg) sacc[ks][cg] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
+    for (int dc = 0; dc < DC; ++dc) {
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int ks = 2 * half + k2;
-          const h8 a = *(const h8*)(kl + (16 * ks + l16) * KSTR + 32 * dc + 8 * lg);
+      for (int ks = 0; ks < 4; ++ks) {
+        const h8 a = *(const h8*)(kl + (16 * ks + l16) * KSTR + 32 * dc + 8 * lg);
 #pragma unroll
-          for (int cg = 0; cg < NCG; ++cg)
-            sacc[k2][cg] =
-                __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[cg][dc], sacc[k2][cg], 0, 0, 0);
-        }
+        for (int cg = 0; cg < NCG; ++cg)
+          sacc[ks][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[cg][dc], sacc[ks][cg], 0, 0, 0);
       }
+    }
 
-      // ---- visibility on flagged tiles ------------------------------------------
-      if (masked) {
+    // ---- visibility on flagged tiles ------------------------------------------
+    if (masked) {
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+      for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int kidx = 32 * half + 16 * k2 + 4 * lg + r;
-            const int2 an = lds.anc[s][kidx];
-            const int u = cur.k0 + kidx;
+        for (int r = 0; r < 4; ++r) {
+          const int kidx = 16 * ks + 4 * lg + r;
+          const int2 an = lds.anc[s][kidx];
+          const int u = cur.k0 + kidx;
 #pragma unroll
-            for (int cg = 0; cg < NCG; ++cg) {
-              const bool vis = (kidx < nk) & (((an.x < ttin[cg]) & (ttin[cg] < an.y)) |
-                                              ((an.x == ttin[cg]) & (u <= trow[cg])));
-              sacc[k2][cg][r] = vis ? sacc[k2][cg][r] : -__builtin_inff();
-            }
+          for (int cg = 0; cg < NCG; ++cg) {
+            const bool vis = (kidx < nk) & (((an.x < ttin[cg]) & (ttin[cg] < an.y)) |
+                                            ((an.x == ttin[cg]) & (u <= trow[cg])));
+            sacc[ks][cg][r] = vis ? sacc[ks][cg][r] : -__builtin_inff();
           }
         }
       }
+    }
 
-      // ---- online softmax with a lazily moved reference max ----------------------
-      // P = exp2(S*c - m) with any m >= the running max minus kRescaleSlack gives
-      // the same normalised result; m is only raised (and O, l rescaled) when a
-      // score exceeds it by more than kRescaleSlack, so P stays <= 2^kRescaleSlack.
-      float mnew[NCG];
-      bool need_any = false;
+    // ---- online softmax with a lazily moved reference max ----------------------
+    // P = exp2(S*c - m) with any m >= the running max minus kRescaleSlack gives
+    // the same normalised result; m is only raised (and O, l rescaled) when a
+    // score exceeds it by more than kRescaleSlack, so P stays <= 2^kRescaleSlack.
+    float mnew[NCG];
+    bool need_any = false;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      float m4[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f4 x = sacc[ks][cg];
+        m4[ks] = max3f(x[0], x[1], fmaxf(x[2], x[3]));
+      }
+      float mx = max3f(m4[0], m4[1], fmaxf(m4[2], m4[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float ms = mx * scale_log2e;
+      const bool need = ms > mrun[cg] + kRescaleSlack;
+      mnew[cg] = need ? ms : mrun[cg];
+      need_any |= need;
+    }
+    if (__any(need_any)) {
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
-        const f4 x = sacc[0][cg], y = sacc[1][cg];
-        float mx = max3f(max3f(x[0], x[1], x[2]), max3f(x[3], y[0], y[1]), fmaxf(y[2], y[3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float ms = mx * scale_log2e;
-        const bool need = ms > mrun[cg] + kRescaleSlack;
-        mnew[cg] = need ? ms : mrun[cg];
-        need_any |= need;
-      }
-      if (__any(need_any)) {
+        const float alpha = __builtin_amdgcn_exp2f(mrun[cg] - mnew[cg]);
+        mrun[cg] = mnew[cg];
+        lacc[cg] *= alpha;
 #pragma unroll
-        for (int cg = 0; cg < NCG; ++cg) {
-          const float alpha = __builtin_amdgcn_exp2f(mrun[cg] - mnew[cg]);
-          mrun[cg] = mnew[cg];
-          lacc[cg] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) oacc[dt][cg] *= alpha;
-        }
+        for (int dt = 0; dt < DT; ++dt) oacc[dt][cg] *= alpha;
       }
+    }
+
+    // ---- P^T and O^T += V^T P^T, one 32-key chunk at a time (the second
+    // chunk's exponentials are independent of the first chunk's MFMAs). The row
+    // sums of P (as rounded to f16, the same P the product uses) come from one
+    // more MFMA against an all-ones A operand. -----------------------------------
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
       h8 pb[NCG];
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
@@ -289,22 +295,18 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
         for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float pv =
-                __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[k2][cg][r], scale_log2e, -mrun[cg]));
+            const float pv = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(sacc[2 * kc + k2][cg][r], scale_log2e, -mrun[cg]));
             pb[cg][k2 * 4 + r] = (_Float16)pv;
           }
         }
       }
-
-      // ---- O^T += V^T P^T over the same 32 keys; the row sums of P (as
-      // rounded to f16, the same P the product uses) come from one more MFMA
-      // against an all-ones A operand ----------------------------------------------
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg)
         lacc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[cg], lacc[cg], 0, 0, 0);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const _Float16* row = vl + (16 * dt + l16) * VSTR + 32 * half + 4 * lg;
+        const _Float16* row = vl + (16 * dt + l16) * VSTR + 32 * kc + 4 * lg;
         const h4 lo = *(const h4*)row;
         const h4 hi = *(const h4*)(row + 16);
         const h8 a = h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -314,7 +316,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
       }
     }
 
-    if (has_next) lstore(s ^ 1, kt + 1);
+    if (has_next) lstore(s ^ 1, nxt);
     __syncthreads();
   }
 
