@@ -33,6 +33,36 @@ if ROOT not in sys.path:
 
 PEAK_F16_TFLOPS = 2516.6   # MI355X dense f16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tree_attn_fwd_traffic.txt")
+KERNEL_SOURCES = ["prefix_tree_packed_amd/csrc/attn_fwd.hip", "prefix_tree_packed_amd/csrc/layout.h",
+                  "prefix_tree_packed_amd/build.py"]
+
+
+def kernel_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config: int, forward: int):
+    """HBM bytes per launch of the attention kernel from the committed profiler
+    record, or None when there is none for this workload or the kernel sources
+    changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            lines = [l.split() for l in fh if l.strip() and not l.startswith("#")]
+    except OSError:
+        return None
+    rec = {l[0]: l[1:] for l in lines if len(l) == 2}
+    if rec.get("kernel_sha256_16", [None])[0] != kernel_hash():
+        return None
+    for l in lines:
+        if len(l) == 6 and l[0] == f"config{config}" and l[1] == f"forward{forward}":
+            return {"fetch_bytes": int(l[3]), "write_bytes": int(l[5])}
+    return None
 
 
 def parse():
@@ -175,9 +205,15 @@ def main():
             "frac": round(achieved / PEAK_F16_TFLOPS, 4),
             "traffic": None,
             "per_launch": {"useful_flop": useful_flops[k], "avg_ms": round(float(attn_ms_mean[k]), 5),
-                           "forward_index": k},
+                           "forward_index": k,
+                           "algorithmic_bytes": algorithmic_bytes(plans[k], wl, args.out_dtype)},
         },
     }
+
+    tr = measured_traffic(args.config, k) if args.seed == 0 and args.out_dtype == "f16" else None
+    if tr is not None:
+        out["roofline"]["traffic"] = tr["fetch_bytes"] + tr["write_bytes"]
+        out["roofline"]["traffic_detail"] = dict(tr, source=os.path.relpath(TRAFFIC_FILE, ROOT))
 
     # correctness guard on the timed outputs (cheap): finite everywhere
     for x in fw:
@@ -194,6 +230,19 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, infos, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def algorithmic_bytes(plan, wl, out_dtype):
+    """Q read and O written once, and every K/V row some query sees read once."""
+    import prefix_tree_packed_amd as P
+    kt = P.tree_attn_plan_schedule(plan)["key_tiles"]
+    seen = np.zeros(plan.info["num_kv_tokens"] + 64, dtype=bool)
+    for k0, n, _ in kt:
+        seen[k0:k0 + n] = True
+    ob = 2 if out_dtype == "f16" else 4
+    q = plan.info["num_q_tokens"] * wl.hq * wl.d
+    kv = 2 * int(seen.sum()) * wl.hkv * wl.d * 2
+    return int(q * 2 + q * ob + kv)
 
 
 def cpu_baseline(wl, infos, seconds):
