@@ -344,6 +344,335 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant. Same work decomposition and arithmetic as
+// tree_attn_fwd_kernel; the K and V tiles travel from global memory straight
+// into LDS (global_load_lds_dwordx4), rows XOR-swizzled at 16-byte granularity
+// so both the K reads and the transposing V reads are bank-conflict free, and
+// the V^T operand of the P.V product is read with ds_read_b64_tr_b16. Three
+// LDS stages let each tile's loads overlap two tiles of math.
+//
+// ds_read_b64_tr_b16 (measured on gfx950): within each group of 16 lanes, lane
+// i receives element (i mod 4) of the 8-byte rows addressed by lanes
+// 4j + floor(i/4) of the group, j = 0..3, as its elements 0..3. So if lane
+// L = 16g + 4j + q points at V[key0 + 4g + j][d0 + 4q .. +3], lane i = 16g + i'
+// receives V[key0 + 4g + j][d0 + i'] for j = 0..3: four consecutive keys of one
+// head-dim column, which is the A-operand layout of the P.V MFMA.
+// ---------------------------------------------------------------------------
+constexpr int kStages = 3;
+
+typedef short s4v __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s4v lds_s4v;
+
+template <int D>
+struct DlLds {
+  static constexpr int ROWB = D * 2;               // bytes per K/V row
+  static constexpr int TILEB = kKeyTile * ROWB;   // bytes per K (or V) tile
+  unsigned char k[kStages][TILEB];
+  unsigned char v[kStages][TILEB];
+  int2 anc[kStages][kKeyTile];
+};
+
+// 16 bytes per lane from global memory straight into LDS at M0 + 16*lane
+// (global_load_lds_dwordx4). Issued as inline asm on purpose: the compiler
+// treats a load-to-LDS it can see as a write to all of LDS and waits for it
+// before every later LDS read, which would stall on the tile being prefetched.
+// These loads are waited for explicitly (wait_vmcnt) before the barrier that
+// publishes their stage. M0 is saved and restored around the load.
+__device__ __forceinline__ void lds_dma16(const void* gptr, unsigned lds_addr) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr));
+}
+
+__device__ __forceinline__ unsigned lds_addr_of(const void* p) {
+  return (unsigned)(uintptr_t)(lds_void*)p;
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding and leaves the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int D, int G, int NCG, int WAVES, bool OUT_F32>
+__global__ void __launch_bounds__(WAVES * 64)
+tree_attn_fwd_dl_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
+                        const _Float16* __restrict__ V, void* __restrict__ Out,
+                        float* __restrict__ Lse, const QTile* __restrict__ qtiles,
+                        const KTile* __restrict__ ktiles, const int* __restrict__ work,
+                        const int2* __restrict__ tok_anc, int hq, int hkv, int n_q_total,
+                        float scale_log2e) {
+  constexpr int DC = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int CPW = 16 * NCG;
+  constexpr int DCH = D / 8;                       // 16-byte chunks per row
+  constexpr int ROWB = DlLds<D>::ROWB;
+  constexpr int RPI = 1024 / ROWB;                 // rows per wave-wide 1 KB load
+  constexpr int IPW = kKeyTile / RPI / WAVES;      // loads per wave per K (or V) tile
+  constexpr int ANCB = kKeyTile * 8 / WAVES;       // anc bytes loaded per wave
+  constexpr int LOADS = 2 * IPW + 1;               // vector-memory ops per wave per tile
+  static_assert(IPW >= 1 && kKeyTile % (RPI * WAVES) == 0, "tile / wave shape");
+  static_assert(ANCB % 16 == 0 && ANCB / 16 <= 64, "anc split");
+
+  __shared__ DlLds<D> lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+
+  const int wid = work[blockIdx.x];
+  const int qt = wid / hkv;
+  const int kvh = wid - qt * hkv;
+  const QTile tile = qtiles[qt];
+  const int ktb = tile.kt_begin, kte = tile.kt_end;
+  if (kte <= ktb) return;  // never planned (a token always sees itself); uniform per workgroup
+
+  // ---- per-lane global offsets of this wave's direct loads -------------------
+  // load j of wave w fills rows (w*IPW + j)*RPI + lane/DCH; the lane's 16 bytes
+  // land in physical chunk lane%DCH, which holds logical chunk
+  // (lane%DCH) ^ (row % DCH).
+  const size_t kv_stride = (size_t)hkv * D;
+  const _Float16* Kh = K + (size_t)kvh * D;
+  const _Float16* Vh = V + (size_t)kvh * D;
+  int lrow[IPW], goff[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int row = (wave * IPW + j) * RPI + lane / DCH;
+    const int chunk = (lane % DCH) ^ (row % DCH);
+    lrow[j] = row;
+    goff[j] = row * (int)kv_stride + 8 * chunk;
+  }
+
+  auto issue = [&](int stage, const KTile& t) {
+    const int nk = t.meta & 0xffff;
+    const _Float16* kb = Kh + (size_t)t.k0 * kv_stride;
+    const _Float16* vb = Vh + (size_t)t.k0 * kv_stride;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      // rows past the tile's keys re-read the tile's first row (finite data;
+      // such rows only occur in flagged tiles, where they get -inf scores)
+      const int off = lrow[j] < nk ? goff[j] : 8 * ((lane % DCH) ^ (lrow[j] % DCH));
+      lds_dma16(kb + off, lds_addr_of(lds.k[stage] + (wave * IPW + j) * 1024));
+      lds_dma16(vb + off, lds_addr_of(lds.v[stage] + (wave * IPW + j) * 1024));
+    }
+    // Euler intervals of the tile's keys (ANCB bytes per wave; the plan pads
+    // tok_anc so a full tile's worth past any k0 is readable)
+    if (lane < ANCB / 16)
+      lds_dma16((const char*)(tok_anc + t.k0) + wave * ANCB + 16 * lane,
+                lds_addr_of((const char*)lds.anc[stage] + wave * ANCB));
+  };
+
+  // ---- columns owned by this lane: (token, head) pairs -------------------
+  int tok[NCG], head[NCG], trow[NCG], ttin[NCG];
+  bool cvalid[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const int c = wave * CPW + cg * 16 + l16;
+    int t = c / G;
+    cvalid[cg] = t < tile.n_tok;
+    t = cvalid[cg] ? t : tile.n_tok - 1;  // padded columns mirror the last token
+    tok[cg] = t;
+    head[cg] = kvh * G + (c % G);
+    trow[cg] = tile.q_row + t;
+    ttin[cg] = tok_anc[trow[cg]].x;
+  }
+
+  // first two tiles in flight before the Q fragments are needed
+  issue(0, ktiles[ktb]);
+  const bool two = ktb + 1 < kte;
+  if (two) issue(1, ktiles[ktb + 1]);
+
+  h8 qf[NCG][DC];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const _Float16* qp = Q + ((size_t)(tile.q_fwd + tok[cg]) * hq + head[cg]) * D + 8 * lg;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) qf[cg][dc] = *(const h8*)(qp + 32 * dc);
+  }
+
+  f4 oacc[DT][NCG];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) oacc[dt][cg] = f4{0.f, 0.f, 0.f, 0.f};
+  float mrun[NCG];
+  f4 lacc[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    mrun[cg] = -1e30f;
+    lacc[cg] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+  const _Float16 one = (_Float16)1.0f;
+  const h8 ones = h8{one, one, one, one, one, one, one, one};
+
+  // lane-constant LDS offsets: K reads (row 16ks + l16, logical chunk 4dc + lg)
+  int koff[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) koff[dc] = l16 * ROWB + (((4 * dc + lg) ^ (l16 % DCH)) * 16);
+  // V transposing reads: lane points at row 4*lg + l16/4 (+ 16*h + 32*kc) and
+  // head-dim 16*dt + 4*(lane%4), i.e. logical chunk 2*dt + (lane%4)/2, byte
+  // 8*(lane%2) inside it; physical chunk = logical ^ (row % DCH). Since 2*dt is
+  // even, (2*dt + b) ^ c = (2*dt ^ (c & ~1)) + ((b ^ c) & 1).
+  const int vr = 4 * lg + (l16 >> 2);
+  const int vq = lane & 3;
+  const int vrs = vr % DCH;
+  const int vbase = vr * ROWB + 16 * (((vq >> 1) ^ vrs) & 1) + 8 * (vq & 1);
+  const int vhi = vrs & ~1;
+
+  // Everything issued so far (both prologue tiles, Q, intervals) was in flight
+  // together; waiting for all of it here costs little and leaves the
+  // compiler with no outstanding loads to wait for inside the loop, where any
+  // wait of its own would also drain the tile being prefetched.
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  for (int kt = ktb; kt < kte; ++kt) {
+    const int s = (kt - ktb) % kStages;
+    const bool more = kt + 2 < kte;  // a tile two ahead exists
+    if (more) issue((kt - ktb + 2) % kStages, ktiles[kt + 2]);
+    const KTile cur = ktiles[kt];
+    const unsigned char* kl = lds.k[s];
+    const unsigned char* vl = lds.v[s];
+    const int nk = cur.meta & 0xffff;
+    const bool masked = (cur.meta & kMaskedBit) != 0;
+
+    f4 sacc[4][NCG];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) sacc[ks][cg] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const h8 a = *(const h8*)(kl + ks * 16 * ROWB + koff[dc]);
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+          sacc[ks][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[cg][dc], sacc[ks][cg], 0, 0, 0);
+      }
+    }
+
+    if (masked) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kidx = 16 * ks + 4 * lg + r;
+          const int2 an = lds.anc[s][kidx];
+          const int u = cur.k0 + kidx;
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg) {
+            const bool vis = (kidx < nk) & (((an.x < ttin[cg]) & (ttin[cg] < an.y)) |
+                                            ((an.x == ttin[cg]) & (u <= trow[cg])));
+            sacc[ks][cg][r] = vis ? sacc[ks][cg][r] : -__builtin_inff();
+          }
+        }
+      }
+    }
+
+    float mnew[NCG];
+    bool need_any = false;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      float m4[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f4 x = sacc[ks][cg];
+        m4[ks] = max3f(x[0], x[1], fmaxf(x[2], x[3]));
+      }
+      float mx = max3f(m4[0], m4[1], fmaxf(m4[2], m4[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float ms = mx * scale_log2e;
+      const bool need = ms > mrun[cg] + kRescaleSlack;
+      mnew[cg] = need ? ms : mrun[cg];
+      need_any |= need;
+    }
+    if (__any(need_any)) {
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
+        const float alpha = __builtin_amdgcn_exp2f(mrun[cg] - mnew[cg]);
+        mrun[cg] = mnew[cg];
+        lacc[cg] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt][cg] *= alpha;
+      }
+    }
+
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      h8 pb[NCG];
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(sacc[2 * kc + k2][cg][r], scale_log2e, -mrun[cg]));
+            pb[cg][k2 * 4 + r] = (_Float16)pv;
+          }
+        }
+      }
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg)
+        lacc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[cg], lacc[cg], 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const unsigned char* base = vl + (32 * kc) * ROWB + vbase + 16 * ((2 * dt) ^ vhi);
+        const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(base));
+        const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(base + 16 * ROWB));
+        h8 a;
+        __builtin_memcpy(&a, &lo, 8);
+        __builtin_memcpy((char*)&a + 8, &hi, 8);
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+          oacc[dt][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[cg], oacc[dt][cg], 0, 0, 0);
+      }
+    }
+
+    // the next tile must have landed (only the tile two ahead may still be in
+    // flight) and every wave must be done with this stage before it is reused
+    if (kt + 1 < kte) {
+      if (more) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const float lt = lacc[cg][0];
+    const float inv = 1.0f / lt;
+    if (!cvalid[cg]) continue;
+    const size_t obase = ((size_t)(tile.q_fwd + tok[cg]) * hq + head[cg]) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const f4 val = oacc[dt][cg] * inv;
+      const int d0 = 16 * dt + 4 * lg;
+      if constexpr (OUT_F32) {
+        *(f4*)((float*)Out + obase + d0) = val;
+      } else {
+        *(h4*)((_Float16*)Out + obase + d0) =
+            h4{(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
+      }
+    }
+    if (Lse != nullptr && lg == 0)
+      Lse[(size_t)head[cg] * n_q_total + tile.q_fwd + tok[cg]] =
+          (mrun[cg] + __log2f(lt)) * 0.69314718055994530942f;
+  }
+}
+
 // Copies this forward's K/V rows into the row-space cache: forward token t
 // goes to cache row tok_rowpos[t]. One thread per 16-byte chunk.
 __global__ void __launch_bounds__(256)
@@ -361,9 +690,15 @@ cache_write_kernel(const _Float16* __restrict__ k_new, const _Float16* __restric
   ((h8*)v_cache)[dst] = ((const h8*)v_new)[src];
 }
 
+#ifndef TA_DIRECT_LDS
+#define TA_DIRECT_LDS 1
+#endif
+
 template <int D, int G, int NCG, int WAVES, bool F32>
 static hipError_t launch_variant(const AttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((tree_attn_fwd_kernel<D, G, NCG, WAVES, F32>), dim3(a.n_work), dim3(WAVES * 64), 0,
+  hipLaunchKernelGGL((TA_DIRECT_LDS ? tree_attn_fwd_dl_kernel<D, G, NCG, WAVES, F32>
+                                    : tree_attn_fwd_kernel<D, G, NCG, WAVES, F32>),
+                     dim3(a.n_work), dim3(WAVES * 64), 0,
                      st, (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v, a.o,
                      a.lse, (const QTile*)a.qtiles, (const KTile*)a.ktiles, (const int*)a.work,
                      (const int2*)a.tok_anc, a.hq, a.hkv, a.n_q, a.scale_log2e);

@@ -208,7 +208,8 @@ void Builder::token_tables() {
   p->tok_block.resize(nq);
   p->tok_offset.resize(nq);
   p->tok_rowpos.resize(nq);
-  p->tok_anc.resize(p->n_kv);
+  // one key tile of padding: the kernel loads a whole tile's intervals from any k0
+  p->tok_anc.assign(p->n_kv + kKeyTile, Int2{0, 0});
   p->useful_pairs = 0;
   p->cost_separate = 0;
   p->leaf_block.clear();
@@ -485,7 +486,7 @@ ta_status tree_attn_plan_schedule(ta_plan_t p, int32_t* q_tiles, int32_t* key_ti
     }
   if (work && !p->work.empty()) memcpy(work, p->work.data(), p->work.size() * sizeof(int32_t));
   if (tok_anc)
-    for (size_t i = 0; i < p->tok_anc.size(); ++i) {
+    for (size_t i = 0; i < (size_t)p->n_kv; ++i) {  // the kernel-side padding is not exported
       tok_anc[2 * i] = p->tok_anc[i].x;
       tok_anc[2 * i + 1] = p->tok_anc[i].y;
     }
