@@ -1,5 +1,5 @@
 // Tree attention forward for gfx950 (MI355X): block-sparse over the schedule
-// built by the host plan, f16 inputs, MFMA f32 accumulation, f32 online
+// built by the host plan, f16 inputs, MFMA with f32 accumulation, f32 online
 // softmax.
 //
 // What it computes: the architecture page "How basal-rs computes a decision",
@@ -8,23 +8,27 @@
 // and section 01, stage "GPU forward pass" (one compact f16 token list,
 // attention with f32 accumulation).
 //
-// Work decomposition. One workgroup (4 wave64s) computes one query tile (up to
-// 64 consecutive row tokens) for one KV head and all query heads that share
-// it. The workgroup's columns are (token, head) pairs, head-minor, so the KV
-// tile staged in LDS is reused by group * tokens query rows. Each wave owns
-// 16*NCG columns and keeps its Q fragments in registers for the whole tile.
+// Work decomposition. One workgroup computes one query tile (up to 64
+// consecutive row tokens) for one KV head and all the query heads that share
+// it. Its columns are (token, head) pairs, head-minor, so each K/V tile staged
+// in LDS serves group * tokens query rows. Each wave owns 16*NCG columns and
+// keeps its Q fragments in registers for the whole tile; at head_dim 128 eight
+// waves of two column groups run two per SIMD.
 //
-// Per 64-key tile (double-buffered in LDS, next tile's global loads issued
-// before the current tile's math):
+// Per 64-key tile (three LDS stages; a tile's loads are issued two tiles
+// ahead of its use, straight from global memory into LDS):
 //   S^T = K Q^T     v_mfma_f32_16x16x32_f16, A = K rows from LDS, B = Q
 //   mask            only on tiles the plan flags: key u is visible to query t
 //                   iff u's block is a proper ancestor of t's block (Euler
 //                   interval test) or the same block with u <= t
-//   softmax         running max per column (two cross-lane steps over the
-//                   4 lane groups that share a column), exp2 with log2(e)
-//                   folded into the scale, running sum kept per lane
-//   O^T += V^T P^T  A = V^T read from an LDS copy stored transposed, B = P^T
-//                   straight from the S^T accumulators (rounded to f16).
+//   softmax         one running reference max per column (two cross-lane steps
+//                   over the 4 lane groups that share a column), moved only
+//                   when a score exceeds it by 2^8; exp2 with log2(e) folded
+//                   into the scale
+//   O^T += V^T P^T  A = V^T read transposed out of row-major LDS
+//                   (ds_read_b64_tr_b16), B = P^T straight from the S^T
+//                   accumulators rounded to f16; the row sums of that P come
+//                   from one more MFMA against an all-ones A operand.
 // Computing the transposed products makes the S^T accumulator layout equal to
 // the B-operand layout the P.V product needs, so P never goes through LDS;
 // the 8 keys a lane holds for one column are {4g..4g+3, 16+4g..16+4g+3} of a
@@ -49,308 +53,13 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return fmaxf(a, fmaxf(b, c));
 }
 
-template <int D>
-struct AttnLds {
-  static constexpr int KSTR = D + 8;  // halves per K row (16-byte pad)
-  static constexpr int VSTR = 68;     // halves per V^T row: 64 keys + 4
-  _Float16 k[2][kKeyTile * KSTR];
-  _Float16 vt[2][D * VSTR];
-  int2 anc[2][kKeyTile];
-};
-
-template <int D, int G, int NCG, int WAVES, bool OUT_F32>
-__global__ void __launch_bounds__(WAVES * 64)
-tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
-                     const _Float16* __restrict__ V, void* __restrict__ Out,
-                     float* __restrict__ Lse, const QTile* __restrict__ qtiles,
-                     const KTile* __restrict__ ktiles, const int* __restrict__ work,
-                     const int2* __restrict__ tok_anc, int hq, int hkv, int n_q_total,
-                     float scale_log2e) {
-  constexpr int DC = D / 32;                 // 32-wide head-dim chunks (QK^T k-steps)
-  constexpr int DT = D / 16;                 // 16-row head-dim tiles (P.V outputs)
-  constexpr int CPW = 16 * NCG;              // columns per wave
-  constexpr int DCH = D / 8;                 // 16-byte chunks per K/V row
-  constexpr int NT = WAVES * 64;             // threads
-  constexpr int RPT = kKeyTile * DCH / NT;   // K rows / V keys per thread
-  constexpr int KSTR = AttnLds<D>::KSTR;
-  constexpr int VSTR = AttnLds<D>::VSTR;
-  static_assert(RPT == 2 || RPT == 4, "unsupported head_dim");
-
-  __shared__ AttnLds<D> lds;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l16 = lane & 15;
-  const int lg = lane >> 4;
-
-  const int wid = work[blockIdx.x];
-  const int qt = wid / hkv;
-  const int kvh = wid - qt * hkv;
-  const QTile tile = qtiles[qt];
-
-  // ---- columns owned by this lane: (token, head) pairs -------------------
-  int tok[NCG], head[NCG], trow[NCG], ttin[NCG];
-  bool cvalid[NCG];
-#pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) {
-    const int c = wave * CPW + cg * 16 + l16;
-    int t = c / G;
-    cvalid[cg] = t < tile.n_tok;
-    t = cvalid[cg] ? t : tile.n_tok - 1;  // padded columns mirror the last token
-    tok[cg] = t;
-    head[cg] = kvh * G + (c % G);
-    trow[cg] = tile.q_row + t;
-    ttin[cg] = tok_anc[trow[cg]].x;
-  }
-
-  // ---- Q fragments (B operand of S^T = K Q^T) ------------------------------
-  h8 qf[NCG][DC];
-#pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) {
-    const _Float16* qp =
-        Q + ((size_t)(tile.q_fwd + tok[cg]) * hq + head[cg]) * D + 8 * lg;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) qf[cg][dc] = *(const h8*)(qp + 32 * dc);
-  }
-
-  f4 oacc[DT][NCG];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) oacc[dt][cg] = f4{0.f, 0.f, 0.f, 0.f};
-  float mrun[NCG];
-  f4 lacc[NCG];  // row sums of P, accumulated by MFMA (every component holds the sum)
-#pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) {
-    mrun[cg] = -1e30f;  // finite: a column whose first tiles are all masked stays NaN-free
-    lacc[cg] = f4{0.f, 0.f, 0.f, 0.f};
-  }
-  const _Float16 one = (_Float16)1.0f;
-  const h8 ones = h8{one, one, one, one, one, one, one, one};
-
-  // ---- K/V staging -------------------------------------------------------
-  // K: thread loads rows krow0 + 16*r (r < RPT) at 16-byte chunk kch, so the
-  //    16 lanes of a row read it contiguously and write it contiguously.
-  // V: thread loads keys vkey0 .. vkey0+RPT-1 at 16-byte chunk vch and stores
-  //    them transposed; consecutive lanes take consecutive key groups, so a
-  //    transposed row segment is written by consecutive lanes (no bank
-  //    conflicts on the V^T stores).
-  const size_t kv_stride = (size_t)hkv * D;
-  const _Float16* Kh = K + (size_t)kvh * D;
-  const _Float16* Vh = V + (size_t)kvh * D;
-  constexpr int VGRP = kKeyTile / RPT;  // key groups per 16-byte column of V
-  const int kch = tid % DCH;
-  const int krow0 = tid / DCH;
-  const int vgrp = tid % VGRP;
-  const int vch = tid / VGRP;
-  const int vkey0 = vgrp * RPT;
-  // loop-invariant parts of the per-lane global offsets (elements)
-  int kofs[RPT], vofs[RPT];
-#pragma unroll
-  for (int r = 0; r < RPT; ++r) {
-    kofs[r] = (krow0 + r * (NT / DCH)) * (int)kv_stride + 8 * kch;
-    vofs[r] = (vkey0 + r) * (int)kv_stride + 8 * vch;
-  }
-  h8 kreg[RPT], vreg[RPT];
-  int2 areg = int2{0, 0};
-
-  // Issue the global loads of key tile `t` into registers. Rows past the tile's
-  // key count read the tile's first row instead: such rows only occur in tiles
-  // flagged for the visibility test, which gives their scores -inf, so their
-  // K never matters and their V is multiplied by an exact 0 (it is finite).
-  // Straight-line loads keep all of them in flight together.
-  auto gload = [&](const KTile& t) {
-    const int nk = t.meta & 0xffff;
-    const _Float16* kb = Kh + (size_t)t.k0 * kv_stride;  // wave-uniform
-    const _Float16* vb = Vh + (size_t)t.k0 * kv_stride;
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      const bool kin = krow0 + r * (NT / DCH) < nk;
-      const bool vin = vkey0 + r < nk;
-      kreg[r] = *(const h8*)(kb + (kin ? kofs[r] : 8 * kch));
-      vreg[r] = *(const h8*)(vb + (vin ? vofs[r] : 8 * vch));
-    }
-    if ((t.meta & kMaskedBit) && tid < kKeyTile) areg = tok_anc[t.k0 + (tid < nk ? tid : 0)];
-  };
-
-  auto lstore = [&](int s, const KTile& t) {
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      const int row = krow0 + r * (NT / DCH);
-      *(h8*)&lds.k[s][row * KSTR + 8 * kch] = kreg[r];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      _Float16* dst = &lds.vt[s][(8 * vch + i) * VSTR + vkey0];
-      if constexpr (RPT == 4) {
-        *(h4*)dst = h4{vreg[0][i], vreg[1][i], vreg[2][i], vreg[3][i]};
-      } else {
-        *(h2*)dst = h2{vreg[0][i], vreg[1][i]};
-      }
-    }
-    if ((t.meta & kMaskedBit) && tid < kKeyTile) lds.anc[s][tid] = areg;
-  };
-
-  const int ktb = tile.kt_begin, kte = tile.kt_end;
-  if (kte <= ktb) return;  // never planned (a token always sees itself); uniform per workgroup
-  KTile nxt = ktiles[ktb];
-  gload(nxt);
-  lstore(0, nxt);
-  __syncthreads();
-
-  for (int kt = ktb; kt < kte; ++kt) {
-    const int s = (kt - ktb) & 1;
-    const KTile cur = nxt;
-    const bool has_next = kt + 1 < kte;
-    if (has_next) {
-      nxt = ktiles[kt + 1];
-      gload(nxt);
-    }
-
-    const _Float16* kl = &lds.k[s][0];
-    const _Float16* vl = &lds.vt[s][0];
-    const int nk = cur.meta & 0xffff;
-    const bool masked = (cur.meta & kMaskedBit) != 0;
-
-    // ---- S^T = K Q^T for the whole 64-key tile --------------------------------
-    f4 sacc[4][NCG];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) sacc[ks][cg] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const h8 a = *(const h8*)(kl + (16 * ks + l16) * KSTR + 32 * dc + 8 * lg);
-#pragma unroll
-        for (int cg = 0; cg < NCG; ++cg)
-          sacc[ks][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[cg][dc], sacc[ks][cg], 0, 0, 0);
-      }
-    }
-
-    // ---- visibility on flagged tiles ------------------------------------------
-    if (masked) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kidx = 16 * ks + 4 * lg + r;
-          const int2 an = lds.anc[s][kidx];
-          const int u = cur.k0 + kidx;
-#pragma unroll
-          for (int cg = 0; cg < NCG; ++cg) {
-            const bool vis = (kidx < nk) & (((an.x < ttin[cg]) & (ttin[cg] < an.y)) |
-                                            ((an.x == ttin[cg]) & (u <= trow[cg])));
-            sacc[ks][cg][r] = vis ? sacc[ks][cg][r] : -__builtin_inff();
-          }
-        }
-      }
-    }
-
-    // ---- online softmax with a lazily moved reference max ----------------------
-    // P = exp2(S*c - m) with any m >= the running max minus kRescaleSlack gives
-    // the same normalised result; m is only raised (and O, l rescaled) when a
-    // score exceeds it by more than kRescaleSlack, so P stays <= 2^kRescaleSlack.
-    float mnew[NCG];
-    bool need_any = false;
-#pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) {
-      float m4[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const f4 x = sacc[ks][cg];
-        m4[ks] = max3f(x[0], x[1], fmaxf(x[2], x[3]));
-      }
-      float mx = max3f(m4[0], m4[1], fmaxf(m4[2], m4[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float ms = mx * scale_log2e;
-      const bool need = ms > mrun[cg] + kRescaleSlack;
-      mnew[cg] = need ? ms : mrun[cg];
-      need_any |= need;
-    }
-    if (__any(need_any)) {
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) {
-        const float alpha = __builtin_amdgcn_exp2f(mrun[cg] - mnew[cg]);
-        mrun[cg] = mnew[cg];
-        lacc[cg] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt][cg] *= alpha;
-      }
-    }
-
-    // ---- P^T and O^T += V^T P^T, one 32-key chunk at a time (the second
-    // chunk's exponentials are independent of the first chunk's MFMAs). The row
-    // sums of P (as rounded to f16, the same P the product uses) come from one
-    // more MFMA against an all-ones A operand. -----------------------------------
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      h8 pb[NCG];
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) {
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(
-                __builtin_fmaf(sacc[2 * kc + k2][cg][r], scale_log2e, -mrun[cg]));
-            pb[cg][k2 * 4 + r] = (_Float16)pv;
-          }
-        }
-      }
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg)
-        lacc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[cg], lacc[cg], 0, 0, 0);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const _Float16* row = vl + (16 * dt + l16) * VSTR + 32 * kc + 4 * lg;
-        const h4 lo = *(const h4*)row;
-        const h4 hi = *(const h4*)(row + 16);
-        const h8 a = h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-        for (int cg = 0; cg < NCG; ++cg)
-          oacc[dt][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[cg], oacc[dt][cg], 0, 0, 0);
-      }
-    }
-
-    if (has_next) lstore(s ^ 1, nxt);
-    __syncthreads();
-  }
-
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2 ------------------------
-#pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) {
-    const float lt = lacc[cg][0];
-    const float inv = 1.0f / lt;
-    if (!cvalid[cg]) continue;
-    const size_t obase = ((size_t)(tile.q_fwd + tok[cg]) * hq + head[cg]) * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const f4 val = oacc[dt][cg] * inv;
-      const int d0 = 16 * dt + 4 * lg;
-      if constexpr (OUT_F32) {
-        *(f4*)((float*)Out + obase + d0) = val;
-      } else {
-        *(h4*)((_Float16*)Out + obase + d0) =
-            h4{(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
-      }
-    }
-    if (Lse != nullptr && lg == 0)
-      Lse[(size_t)head[cg] * n_q_total + tile.q_fwd + tok[cg]] =
-          (mrun[cg] + __log2f(lt)) * 0.69314718055994530942f;
-  }
-}
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS variant. Same work decomposition and arithmetic as
-// tree_attn_fwd_kernel; the K and V tiles travel from global memory straight
-// into LDS (global_load_lds_dwordx4), rows XOR-swizzled at 16-byte granularity
-// so both the K reads and the transposing V reads are bank-conflict free, and
-// the V^T operand of the P.V product is read with ds_read_b64_tr_b16. Three
-// LDS stages let each tile's loads overlap two tiles of math.
+// Data movement. The K and V tiles travel from global memory straight into LDS
+// (global_load_lds_dwordx4), rows XOR-swizzled at 16-byte granularity so both
+// the K reads and the transposing V reads are bank-conflict free, and the V^T
+// operand of the P.V product is read with ds_read_b64_tr_b16. Three LDS stages
+// let each tile's loads overlap two tiles of math.
 //
 // ds_read_b64_tr_b16 (measured on gfx950): within each group of 16 lanes, lane
 // i receives element (i mod 4) of the 8-byte rows addressed by lanes
@@ -359,6 +68,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
 // receives V[key0 + 4g + j][d0 + i'] for j = 0..3: four consecutive keys of one
 // head-dim column, which is the A-operand layout of the P.V MFMA.
 // ---------------------------------------------------------------------------
+// LDS stages: a tile's loads are issued two tiles ahead of its use.
 constexpr int kStages = 3;
 
 typedef short s4v __attribute__((__vector_size__(4 * sizeof(short))));
@@ -405,7 +115,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <int D, int G, int NCG, int WAVES, bool OUT_F32>
 __global__ void __launch_bounds__(WAVES * 64)
-tree_attn_fwd_dl_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
+tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                         const _Float16* __restrict__ V, void* __restrict__ Out,
                         float* __restrict__ Lse, const QTile* __restrict__ qtiles,
                         const KTile* __restrict__ ktiles, const int* __restrict__ work,
@@ -537,13 +247,35 @@ tree_attn_fwd_dl_kernel(const _Float16* __restrict__ Q, const _Float16* __restri
   wait_vmcnt<0>();
   __syncthreads();
 
+  auto pv_product = [&](int stage, const h8 (&pb)[2][NCG]) {
+    const unsigned char* vl = lds.v[stage];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg)
+        lacc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[kc][cg], lacc[cg], 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const unsigned char* base = vl + (32 * kc) * ROWB + vbase + 16 * ((2 * dt) ^ vhi);
+        const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(base));
+        const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(base + 16 * ROWB));
+        h8 av;
+        __builtin_memcpy(&av, &lo, 8);
+        __builtin_memcpy((char*)&av + 8, &hi, 8);
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+          oacc[dt][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[kc][cg], oacc[dt][cg], 0, 0, 0);
+      }
+    }
+  };
+
   for (int kt = ktb; kt < kte; ++kt) {
     const int s = (kt - ktb) % kStages;
     const bool more = kt + 2 < kte;  // a tile two ahead exists
     if (more) issue((kt - ktb + 2) % kStages, ktiles[kt + 2]);
     const KTile cur = ktiles[kt];
+
     const unsigned char* kl = lds.k[s];
-    const unsigned char* vl = lds.v[s];
     const int nk = cur.meta & 0xffff;
     const bool masked = (cur.meta & kMaskedBit) != 0;
 
@@ -610,37 +342,18 @@ tree_attn_fwd_dl_kernel(const _Float16* __restrict__ Q, const _Float16* __restri
       }
     }
 
+    h8 pb[2][NCG];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      h8 pb[NCG];
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) {
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(
-                __builtin_fmaf(sacc[2 * kc + k2][cg][r], scale_log2e, -mrun[cg]));
-            pb[cg][k2 * 4 + r] = (_Float16)pv;
-          }
-        }
-      }
+    for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg)
-        lacc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[cg], lacc[cg], 0, 0, 0);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const unsigned char* base = vl + (32 * kc) * ROWB + vbase + 16 * ((2 * dt) ^ vhi);
-        const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(base));
-        const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(base + 16 * ROWB));
-        h8 a;
-        __builtin_memcpy(&a, &lo, 8);
-        __builtin_memcpy((char*)&a + 8, &hi, 8);
+        for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int cg = 0; cg < NCG; ++cg)
-          oacc[dt][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[cg], oacc[dt][cg], 0, 0, 0);
-      }
-    }
+          for (int r = 0; r < 4; ++r)
+            pb[kc][cg][k2 * 4 + r] = (_Float16)__builtin_amdgcn_exp2f(
+                __builtin_fmaf(sacc[2 * kc + k2][cg][r], scale_log2e, -mrun[cg]));
+    pv_product(s, pb);
 
     // the next tile must have landed (only the tile two ahead may still be in
     // flight) and every wave must be done with this stage before it is reused
@@ -690,14 +403,9 @@ cache_write_kernel(const _Float16* __restrict__ k_new, const _Float16* __restric
   ((h8*)v_cache)[dst] = ((const h8*)v_new)[src];
 }
 
-#ifndef TA_DIRECT_LDS
-#define TA_DIRECT_LDS 1
-#endif
-
 template <int D, int G, int NCG, int WAVES, bool F32>
 static hipError_t launch_variant(const AttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((TA_DIRECT_LDS ? tree_attn_fwd_dl_kernel<D, G, NCG, WAVES, F32>
-                                    : tree_attn_fwd_kernel<D, G, NCG, WAVES, F32>),
+  hipLaunchKernelGGL((tree_attn_fwd_kernel<D, G, NCG, WAVES, F32>),
                      dim3(a.n_work), dim3(WAVES * 64), 0,
                      st, (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v, a.o,
                      a.lse, (const QTile*)a.qtiles, (const KTile*)a.ktiles, (const int*)a.work,
