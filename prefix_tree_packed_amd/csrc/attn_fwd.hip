@@ -53,6 +53,18 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return fmaxf(a, fmaxf(b, c));
 }
 
+// Maximum over the four lanes l, l^16, l^32, l^48 that hold one column: two
+// in-VALU lane swaps (permlane32_swap exchanges the wave's halves,
+// permlane16_swap the 16-lane rows within each half), no LDS round trip.
+__device__ __forceinline__ float column_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const unsigned v = __float_as_uint(y);
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 
 // ---------------------------------------------------------------------------
 // Data movement. The K and V tiles travel from global memory straight into LDS
@@ -137,7 +149,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l16 = lane & 15;
   const int lg = lane >> 4;
 
@@ -269,10 +281,10 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     }
   };
 
+  int s = 0, s2 = 2;  // stages of tile kt and of tile kt + 2
   for (int kt = ktb; kt < kte; ++kt) {
-    const int s = (kt - ktb) % kStages;
     const bool more = kt + 2 < kte;  // a tile two ahead exists
-    if (more) issue((kt - ktb + 2) % kStages, ktiles[kt + 2]);
+    if (more) issue(s2, ktiles[kt + 2]);
     const KTile cur = ktiles[kt];
 
     const unsigned char* kl = lds.k[s];
@@ -323,9 +335,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
         const f4 x = sacc[ks][cg];
         m4[ks] = max3f(x[0], x[1], fmaxf(x[2], x[3]));
       }
-      float mx = max3f(m4[0], m4[1], fmaxf(m4[2], m4[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mx = column_max(max3f(m4[0], m4[1], fmaxf(m4[2], m4[3])));
       const float ms = mx * scale_log2e;
       const bool need = ms > mrun[cg] + kRescaleSlack;
       mnew[cg] = need ? ms : mrun[cg];
@@ -361,6 +371,8 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
       if (more) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
     }
     __syncthreads();
+    s = s == kStages - 1 ? 0 : s + 1;
+    s2 = s2 == kStages - 1 ? 0 : s2 + 1;
   }
 
 #pragma unroll
