@@ -148,6 +148,11 @@ ta_status tree_attn_plan_info(ta_plan_t plan, ta_plan_info* out);
  * call returns once the host-side tables may be freed (the copy itself is
  * ordered on the stream). A plan may be uploaded again (e.g. to another
  * workspace); forwards use the latest upload.
+ * The attention kernel runs persistent workgroups: the upload sizes the grid
+ * for the current device (as many workgroups as fit on it at once, at most
+ * the number of work items and at most the cap set with
+ * tree_attn_plan_set_max_workgroups) and stores each workgroup's list of work
+ * items, as tree_attn_plan_workgroups computes them, in the workspace.
  * Errors: TA_ERR_INVALID_ARGUMENT, TA_ERR_WORKSPACE, TA_ERR_HIP.
  */
 ta_status tree_attn_plan_upload(ta_plan_t plan, void* d_workspace, size_t bytes, void* hip_stream);
@@ -172,13 +177,39 @@ ta_status tree_attn_plan_export(ta_plan_t plan, int32_t* pos_id, int32_t* tok_ro
  *           end key tile)
  *   key_tiles [num_key_tiles * 3]: per key tile (row-space first key, keys,
  *           1 if the kernel applies the per-key visibility test, else 0)
- *   work [num_work_items]: launch order, query_tile * num_kv_heads + kv_head
- *   tok_anc [num_kv_tokens * 2]: per row-space token, the Euler interval
- *           [tin, tout) of its block over the forest; key u is visible to
- *           query t iff tin(u) < tin(t) < tout(u), or tin(u) == tin(t) and u <= t
+ *   work [num_work_items]: the work items longest first, each query_tile *
+ *           num_kv_heads + kv_head, the KV heads of one tile together
+ *   tok_anc [num_kv_tokens * 2]: per row-space token u, (P(u), E(u)): P is
+ *           u's position when the forest's blocks are visited in pre-order
+ *           and each block's tokens in order, E is the end (exclusive) of
+ *           u's block's subtree in that numbering; key u is visible to query
+ *           t iff P(u) <= P(t) < E(u)
  */
 ta_status tree_attn_plan_schedule(ta_plan_t plan, int32_t* q_tiles, int32_t* key_tiles,
                                   int32_t* work, int32_t* tok_anc);
+
+/*
+ * Cap the number of persistent workgroups later uploads may launch (0, the
+ * default: no cap; at most 8192), e.g. to leave compute units to other work.
+ * Takes effect at the next tree_attn_plan_upload. Host only.
+ * Errors: TA_ERR_INVALID_ARGUMENT (NULL plan, cap out of range).
+ */
+ta_status tree_attn_plan_set_max_workgroups(ta_plan_t plan, int32_t max_workgroups);
+
+/*
+ * Host copy of how the work items would be split over `n_wg` persistent
+ * workgroups (1 <= n_wg <= 8192): workgroup w runs the items
+ * wg_items[wg_ptr[w] .. wg_ptr[w+1]) in that order, each item once over all
+ * workgroups. Items go longest-first to the workgroup with the least work so
+ * far (weighted key tiles plus one per item); when num_kv_heads and n_wg are
+ * both multiples of 8 (the XCD count), the items of KV head h only go to
+ * workgroups w = h (mod 8), which the hardware places on one XCD, so each
+ * XCD's L2 holds the K/V of its own heads only.
+ *   wg_ptr [n_wg + 1]   wg_items [num_work_items] (caller-allocated)
+ * Errors: TA_ERR_INVALID_ARGUMENT (NULL pointer, n_wg out of range).
+ */
+ta_status tree_attn_plan_workgroups(ta_plan_t plan, int32_t n_wg, int32_t* wg_ptr,
+                                    int32_t* wg_items);
 
 /* Free the plan's host memory. The device workspace stays the caller's. NULL is a no-op. */
 ta_status tree_attn_plan_destroy(ta_plan_t plan);

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "TA_OK", 1: "TA_ERR_INVALID_ARGUMENT", 2: "TA_ERR_INVALID_TRE
 TA_F16, TA_F32 = 0, 1
 
 EXPORTED = ("tree_attn_plan", "tree_attn_plan_info", "tree_attn_plan_upload",
-            "tree_attn_plan_export", "tree_attn_plan_schedule", "tree_attn_plan_destroy", "tree_attn_forward",
+            "tree_attn_plan_export", "tree_attn_plan_schedule", "tree_attn_plan_set_max_workgroups",
+            "tree_attn_plan_workgroups", "tree_attn_plan_destroy", "tree_attn_forward",
             "tree_attn_forward_chunked", "tree_attn_cache_write", "tree_attn_forward_cached",
             "decision_readout", "tree_attn_last_error")
 
@@ -82,6 +83,8 @@ def load_library(path: str = LIB_PATH):
     lib.tree_attn_plan_upload.argtypes = [vp, vp, ctypes.c_size_t, vp]
     lib.tree_attn_plan_export.argtypes = [vp, p32, p32, p32, p32, p32, p32]
     lib.tree_attn_plan_schedule.argtypes = [vp, p32, p32, p32, p32]
+    lib.tree_attn_plan_set_max_workgroups.argtypes = [vp, i32]
+    lib.tree_attn_plan_workgroups.argtypes = [vp, i32, p32, p32]
     lib.tree_attn_plan_destroy.argtypes = [vp]
     lib.tree_attn_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.tree_attn_forward_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, vp, vp]
@@ -203,8 +206,8 @@ def tree_attn_plan_export(plan: Plan) -> dict:
 
 
 def tree_attn_plan_schedule(plan: Plan) -> dict:
-    """Host copy of the block-sparse schedule (query tiles, key tiles, launch
-    order, per-token Euler intervals)."""
+    """Host copy of the block-sparse schedule (query tiles, key tiles, work
+    items longest first, per-token pre-order positions and subtree ends)."""
     info = plan.info
     out = {"q_tiles": np.zeros((info["num_q_tiles"], 5), np.int32),
            "key_tiles": np.zeros((info["num_key_tiles"], 3), np.int32),
@@ -213,6 +216,21 @@ def tree_attn_plan_schedule(plan: Plan) -> dict:
     _check(load_library().tree_attn_plan_schedule(
         plan.handle, _ptr32(out["q_tiles"]), _ptr32(out["key_tiles"]), _ptr32(out["work"]),
         _ptr32(out["tok_anc"])))
+    return out
+
+
+def tree_attn_plan_set_max_workgroups(plan: Plan, max_workgroups: int) -> None:
+    """Cap the persistent grid of later uploads (0: no cap)."""
+    _check(load_library().tree_attn_plan_set_max_workgroups(plan.handle, int(max_workgroups)))
+
+
+def tree_attn_plan_workgroups(plan: Plan, n_wg: int) -> dict:
+    """Host copy of the split of the work items over n_wg persistent workgroups:
+    workgroup w runs wg_items[wg_ptr[w]:wg_ptr[w + 1]]."""
+    out = {"wg_ptr": np.zeros(max(int(n_wg), 0) + 1, np.int32),
+           "wg_items": np.zeros(plan.info["num_work_items"], np.int32)}
+    _check(load_library().tree_attn_plan_workgroups(plan.handle, int(n_wg), _ptr32(out["wg_ptr"]),
+                                                    _ptr32(out["wg_items"])))
     return out
 
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -39,14 +41,15 @@ static AttnArgs attn_args(ta_plan_t p, const void* q, const void* k, const void*
   a.lse = lse;
   a.qtiles = ws + p->off_qtiles;
   a.ktiles = ws + p->off_ktiles;
-  a.work = ws + p->off_work;
+  a.wg_ptr = ws + p->off_wg_ptr;
+  a.wg_items = ws + p->off_wg_items;
   a.tok_anc = ws + p->off_anc;
   a.hq = p->cfg.num_q_heads;
   a.hkv = p->cfg.num_kv_heads;
   a.head_dim = p->cfg.head_dim;
   a.group = p->group;
   a.n_q = (int)p->n_q;
-  a.n_work = (int)p->work.size();
+  a.n_wg = p->n_wg;
   a.scale_log2e = p->cfg.scale * 1.4426950408889634f;
   a.out_f32 = p->cfg.out_dtype == TA_F32;
   return a;
@@ -62,8 +65,23 @@ ta_status tree_attn_plan_upload(ta_plan_t p, void* d_workspace, size_t bytes, vo
   if (bytes < p->ws_bytes)
     return ta::fail(TA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", bytes, p->ws_bytes);
   if ((uintptr_t)d_workspace & 255u) return ta::fail(TA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  hipError_t e = hipMemcpyAsync(d_workspace, p->image.data(), p->ws_bytes, hipMemcpyHostToDevice,
-                                (hipStream_t)hip_stream);
+  // persistent grid: every workgroup that fits on the current device at once,
+  // no more than there are work items (and no more than the caller's cap)
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return ta::hip_fail(e, "querying the device");
+  const int per_cu = ta::attention_blocks_per_cu(p->cfg.head_dim, p->group, p->cfg.out_dtype == TA_F32);
+  if (per_cu < 1) return ta::fail(TA_ERR_HIP, "attention kernel does not fit on a compute unit");
+  long long n_wg = std::min<long long>((long long)cus * per_cu, ta::kMaxWorkgroups);
+  if (p->max_workgroups > 0) n_wg = std::min<long long>(n_wg, p->max_workgroups);
+  n_wg = std::min<long long>(n_wg, (long long)p->work.size());
+  p->n_wg = (int)n_wg;
+  if (n_wg > 0)
+    ta::assign_workgroups(p, p->n_wg, (int32_t*)(p->image.data() + p->off_wg_ptr),
+                          (int32_t*)(p->image.data() + p->off_wg_items));
+  e = hipMemcpyAsync(d_workspace, p->image.data(), p->ws_bytes, hipMemcpyHostToDevice,
+                     (hipStream_t)hip_stream);
   if (e != hipSuccess) return ta::hip_fail(e, "plan upload");
   p->d_ws = d_workspace;
   return TA_OK;

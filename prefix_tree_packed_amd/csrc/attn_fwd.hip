@@ -19,8 +19,9 @@
 // ahead of its use, straight from global memory into LDS):
 //   S^T = K Q^T     v_mfma_f32_16x16x32_f16, A = K rows from LDS, B = Q
 //   mask            only on tiles the plan flags: key u is visible to query t
-//                   iff u's block is a proper ancestor of t's block (Euler
-//                   interval test) or the same block with u <= t
+//                   iff u's block is a proper ancestor of t's block or the
+//                   same block with u <= t, tested as P(u) <= P(t) < E(u) on
+//                   the plan's token pre-order positions P and subtree ends E
 //   softmax         one running reference max per column (two cross-lane steps
 //                   over the 4 lane groups that share a column), moved only
 //                   when a score exceeds it by 2^8; exp2 with log2(e) folded
@@ -68,10 +69,18 @@ __device__ __forceinline__ float column_max(float x) {
 
 // ---------------------------------------------------------------------------
 // Data movement. The K and V tiles travel from global memory straight into LDS
-// (global_load_lds_dwordx4), rows XOR-swizzled at 16-byte granularity so both
-// the K reads and the transposing V reads are bank-conflict free, and the V^T
-// operand of the P.V product is read with ds_read_b64_tr_b16. Three LDS stages
-// let each tile's loads overlap two tiles of math.
+// (global_load_lds_dwordx4), rows XOR-swizzled at 16-byte granularity, and the
+// V^T operand of the P.V product is read with ds_read_b64_tr_b16. Three LDS
+// stages let each tile's loads overlap two tiles of math.
+//
+// The two tiles use different swizzles because they are read differently. A K
+// read (ds_read_b128) has 16 lanes fetch one logical chunk of 16 consecutive
+// rows, so K chunk c of row r sits at physical chunk c ^ (r mod DCH). A V read
+// has each 16-lane group fetch the two chunks {2t, 2t+1} of four consecutive
+// rows; with the K swizzle rows r and r^1 would land on the same two chunk
+// positions (a 2-way bank conflict on every V read), so V chunk c of row r sits
+// at c ^ v_swizzle(r), which spreads those eight chunks over eight distinct
+// positions (and over sixteen for two adjacent groups at head_dim 128).
 //
 // ds_read_b64_tr_b16 (measured on gfx950): within each group of 16 lanes, lane
 // i receives element (i mod 4) of the 8-byte rows addressed by lanes
@@ -80,8 +89,9 @@ __device__ __forceinline__ float column_max(float x) {
 // receives V[key0 + 4g + j][d0 + i'] for j = 0..3: four consecutive keys of one
 // head-dim column, which is the A-operand layout of the P.V MFMA.
 // ---------------------------------------------------------------------------
-// LDS stages: a tile's loads are issued two tiles ahead of its use.
-constexpr int kStages = 3;
+// LDS stages: a tile's loads are issued three tiles ahead of its P.V product
+// (two ahead of its S product). A power of two.
+constexpr int kStages = 4;
 
 typedef short s4v __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -117,6 +127,13 @@ __device__ __forceinline__ unsigned lds_addr_of(const void* p) {
   return (unsigned)(uintptr_t)(lds_void*)p;
 }
 
+// Physical-chunk XOR of V row r: 2*(r mod 4) in bits 1-2 and bit 2 of r in
+// bit 3, cut to the row's DCH chunks. Always even; depends on r mod 8 only.
+template <int DCH>
+__device__ __forceinline__ int v_swizzle(int r) {
+  return ((2 * (r & 3)) | (((r >> 2) & 1) << 3)) & (DCH - 1);
+}
+
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding and leaves the other counters alone (gfx9 encoding).
 template <int N>
@@ -130,9 +147,9 @@ __global__ void __launch_bounds__(WAVES * 64)
 tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                         const _Float16* __restrict__ V, void* __restrict__ Out,
                         float* __restrict__ Lse, const QTile* __restrict__ qtiles,
-                        const KTile* __restrict__ ktiles, const int* __restrict__ work,
-                        const int2* __restrict__ tok_anc, int hq, int hkv, int n_q_total,
-                        float scale_log2e) {
+                        const KTile* __restrict__ ktiles, const int* __restrict__ wg_ptr,
+                        const int* __restrict__ wg_items, const int2* __restrict__ tok_anc, int hq,
+                        int hkv, int n_q_total, float scale_log2e) {
   constexpr int DC = D / 32;
   constexpr int DT = D / 16;
   constexpr int CPW = 16 * NCG;
@@ -153,88 +170,99 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   const int l16 = lane & 15;
   const int lg = lane >> 4;
 
-  const int wid = work[blockIdx.x];
-  const int qt = wid / hkv;
-  const int kvh = wid - qt * hkv;
-  const QTile tile = qtiles[qt];
-  const int ktb = tile.kt_begin, kte = tile.kt_end;
-  if (kte <= ktb) return;  // never planned (a token always sees itself); uniform per workgroup
+  // this workgroup's work items (query tile, KV head), in order
+  const int ib = wg_ptr[blockIdx.x], ie = wg_ptr[blockIdx.x + 1];
+  if (ie <= ib) return;  // uniform per workgroup
 
   // ---- per-lane global offsets of this wave's direct loads -------------------
   // load j of wave w fills rows (w*IPW + j)*RPI + lane/DCH; the lane's 16 bytes
   // land in physical chunk lane%DCH, which holds logical chunk
-  // (lane%DCH) ^ (row % DCH).
+  // (lane%DCH) ^ (row % DCH) (K) or (lane%DCH) ^ v_swizzle(row) (V).
   const size_t kv_stride = (size_t)hkv * D;
-  const _Float16* Kh = K + (size_t)kvh * D;
-  const _Float16* Vh = V + (size_t)kvh * D;
-  int lrow[IPW], goff[IPW];
+  int lrow[IPW], kch[IPW], vch[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
     const int row = (wave * IPW + j) * RPI + lane / DCH;
-    const int chunk = (lane % DCH) ^ (row % DCH);
     lrow[j] = row;
-    goff[j] = row * (int)kv_stride + 8 * chunk;
+    kch[j] = 8 * ((lane % DCH) ^ (row % DCH));
+    vch[j] = 8 * ((lane % DCH) ^ v_swizzle<DCH>(row));
   }
 
-  auto issue = [&](int stage, const KTile& t) {
+  auto issue = [&](int stage, int kvh, const KTile& t) {
     const int nk = t.meta & 0xffff;
-    const _Float16* kb = Kh + (size_t)t.k0 * kv_stride;
-    const _Float16* vb = Vh + (size_t)t.k0 * kv_stride;
+    const _Float16* kb = K + (size_t)kvh * D + (size_t)t.k0 * kv_stride;
+    const _Float16* vb = V + (size_t)kvh * D + (size_t)t.k0 * kv_stride;
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
       // rows past the tile's keys re-read the tile's first row (finite data;
       // such rows only occur in flagged tiles, where they get -inf scores)
-      const int off = lrow[j] < nk ? goff[j] : 8 * ((lane % DCH) ^ (lrow[j] % DCH));
-      lds_dma16(kb + off, lds_addr_of(lds.k[stage] + (wave * IPW + j) * 1024));
-      lds_dma16(vb + off, lds_addr_of(lds.v[stage] + (wave * IPW + j) * 1024));
+      const int roff = lrow[j] < nk ? lrow[j] * (int)kv_stride : 0;
+      lds_dma16(kb + roff + kch[j], lds_addr_of(lds.k[stage] + (wave * IPW + j) * 1024));
+      lds_dma16(vb + roff + vch[j], lds_addr_of(lds.v[stage] + (wave * IPW + j) * 1024));
     }
-    // Euler intervals of the tile's keys (ANCB bytes per wave; the plan pads
-    // tok_anc so a full tile's worth past any k0 is readable)
+    // (P, E) of the tile's keys (ANCB bytes per wave; the plan pads tok_anc so
+    // a full tile's worth past any k0 is readable)
     if (lane < ANCB / 16)
       lds_dma16((const char*)(tok_anc + t.k0) + wave * ANCB + 16 * lane,
                 lds_addr_of((const char*)lds.anc[stage] + wave * ANCB));
   };
 
-  // ---- columns owned by this lane: (token, head) pairs -------------------
-  int tok[NCG], head[NCG], trow[NCG], ttin[NCG];
-  bool cvalid[NCG];
-#pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) {
-    const int c = wave * CPW + cg * 16 + l16;
-    int t = c / G;
-    cvalid[cg] = t < tile.n_tok;
-    t = cvalid[cg] ? t : tile.n_tok - 1;  // padded columns mirror the last token
-    tok[cg] = t;
-    head[cg] = kvh * G + (c % G);
-    trow[cg] = tile.q_row + t;
-    ttin[cg] = tok_anc[trow[cg]].x;
-  }
+  // Load cursor: the workgroup's key tiles as one sequence over its items.
+  // Every tile consumed issues the tile three places further on (which may
+  // belong to a later item), so item boundaries do not drain the pipeline.
+  int l_pos = ib, l_kt = 0, l_kte = 0, l_kvh = 0, l_stage = 0;
+  auto l_open = [&]() {
+    const int w = wg_items[l_pos];
+    const int qt = w / hkv;
+    l_kvh = w - qt * hkv;
+    l_kt = qtiles[qt].kt_begin;
+    l_kte = qtiles[qt].kt_end;  // > kt_begin: a token always sees itself
+  };
+  l_open();
+  auto issue_next = [&]() {
+    if (l_pos >= ie) return false;
+    issue(l_stage, l_kvh, ktiles[l_kt]);
+    l_stage = (l_stage + 1) & (kStages - 1);
+    if (++l_kt >= l_kte && ++l_pos < ie) l_open();
+    return true;
+  };
 
-  // first two tiles in flight before the Q fragments are needed
-  issue(0, ktiles[ktb]);
-  const bool two = ktb + 1 < kte;
-  if (two) issue(1, ktiles[ktb + 1]);
-
+  // ---- the item being computed: its query tile and the lane's columns ------
+  // Column c of a tile is (token c / G, head kvh * G + c % G); padded columns
+  // (token >= n_tok) mirror the tile's last token and are not stored. Columns
+  // are recomputed from the tile where needed rather than kept in registers.
+  int c_kvh = 0;
+  QTile tile;
+  int tpos[NCG];
   h8 qf[NCG][DC];
+  auto col_token = [&](int cg, int n_tok) { return min((wave * CPW + cg * 16 + l16) / G, n_tok - 1); };
+  auto col_head = [&](int cg, int kvh) { return kvh * G + (wave * CPW + cg * 16 + l16) % G; };
+  // Opens item `pos`: its tile, the columns' pre-order positions and the Q
+  // fragments (loads left in flight).
+  auto open_item = [&](int pos) {
+    const int w = wg_items[pos];
+    const int qt = w / hkv;
+    c_kvh = w - qt * hkv;
+    tile = qtiles[qt];
 #pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) {
-    const _Float16* qp = Q + ((size_t)(tile.q_fwd + tok[cg]) * hq + head[cg]) * D + 8 * lg;
+    for (int cg = 0; cg < NCG; ++cg) {
+      const int t = col_token(cg, tile.n_tok);
+      tpos[cg] = tok_anc[tile.q_row + t].x;
+      const _Float16* qp = Q + ((size_t)(tile.q_fwd + t) * hq + col_head(cg, c_kvh)) * D + 8 * lg;
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) qf[cg][dc] = *(const h8*)(qp + 32 * dc);
-  }
+      for (int dc = 0; dc < DC; ++dc) qf[cg][dc] = *(const h8*)(qp + 32 * dc);
+    }
+  };
+
+  // first three tiles in flight together with the first item's Q fragments
+  issue_next();
+  issue_next();
+  issue_next();
+  open_item(ib);
 
   f4 oacc[DT][NCG];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) oacc[dt][cg] = f4{0.f, 0.f, 0.f, 0.f};
   float mrun[NCG];
   f4 lacc[NCG];
-#pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) {
-    mrun[cg] = -1e30f;
-    lacc[cg] = f4{0.f, 0.f, 0.f, 0.f};
-  }
   const _Float16 one = (_Float16)1.0f;
   const h8 ones = h8{one, one, one, one, one, one, one, one};
 
@@ -244,54 +272,23 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   for (int dc = 0; dc < DC; ++dc) koff[dc] = l16 * ROWB + (((4 * dc + lg) ^ (l16 % DCH)) * 16);
   // V transposing reads: lane points at row 4*lg + l16/4 (+ 16*h + 32*kc) and
   // head-dim 16*dt + 4*(lane%4), i.e. logical chunk 2*dt + (lane%4)/2, byte
-  // 8*(lane%2) inside it; physical chunk = logical ^ (row % DCH). Since 2*dt is
-  // even, (2*dt + b) ^ c = (2*dt ^ (c & ~1)) + ((b ^ c) & 1).
+  // 8*(lane%2) inside it; physical chunk = logical ^ v_swizzle(row), where the
+  // swizzle depends on row mod 8 only and is even, so the physical chunk is
+  // (2*dt ^ v_swizzle(row)) + (lane%4)/2.
   const int vr = 4 * lg + (l16 >> 2);
-  const int vq = lane & 3;
-  const int vrs = vr % DCH;
-  const int vbase = vr * ROWB + 16 * (((vq >> 1) ^ vrs) & 1) + 8 * (vq & 1);
-  const int vhi = vrs & ~1;
+  const int vbase = vr * ROWB + 8 * (lane & 3);
+  const int vsw = v_swizzle<DCH>(vr);
 
-  // Everything issued so far (both prologue tiles, Q, intervals) was in flight
+  // Everything issued so far (the first tiles, Q, positions) was in flight
   // together; waiting for all of it here costs little and leaves the
   // compiler with no outstanding loads to wait for inside the loop, where any
   // wait of its own would also drain the tile being prefetched.
   wait_vmcnt<0>();
   __syncthreads();
 
-  auto pv_product = [&](int stage, const h8 (&pb)[2][NCG]) {
-    const unsigned char* vl = lds.v[stage];
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg)
-        lacc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[kc][cg], lacc[cg], 0, 0, 0);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const unsigned char* base = vl + (32 * kc) * ROWB + vbase + 16 * ((2 * dt) ^ vhi);
-        const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(base));
-        const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(base + 16 * ROWB));
-        h8 av;
-        __builtin_memcpy(&av, &lo, 8);
-        __builtin_memcpy((char*)&av + 8, &hi, 8);
-#pragma unroll
-        for (int cg = 0; cg < NCG; ++cg)
-          oacc[dt][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[kc][cg], oacc[dt][cg], 0, 0, 0);
-      }
-    }
-  };
-
-  int s = 0, s2 = 2;  // stages of tile kt and of tile kt + 2
-  for (int kt = ktb; kt < kte; ++kt) {
-    const bool more = kt + 2 < kte;  // a tile two ahead exists
-    if (more) issue(s2, ktiles[kt + 2]);
-    const KTile cur = ktiles[kt];
-
-    const unsigned char* kl = lds.k[s];
-    const int nk = cur.meta & 0xffff;
-    const bool masked = (cur.meta & kMaskedBit) != 0;
-
-    f4 sacc[4][NCG];
+  // S^T of one key tile: K rows from LDS (A) against the Q fragments (B)
+  auto s_product = [&](int stage, f4 (&sacc)[4][NCG]) {
+    const unsigned char* kl = lds.k[stage];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -306,27 +303,29 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
           sacc[ks][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[cg][dc], sacc[ks][cg], 0, 0, 0);
       }
     }
+  };
 
-    if (masked) {
+  // -inf for keys query t must not see (flagged tiles only)
+  auto apply_mask = [&](int stage, const KTile& t, f4 (&sacc)[4][NCG]) {
+    const int nk = t.meta & 0xffff;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kidx = 16 * ks + 4 * lg + r;
-          const int2 an = lds.anc[s][kidx];
-          const int u = cur.k0 + kidx;
+      for (int r = 0; r < 4; ++r) {
+        const int kidx = 16 * ks + 4 * lg + r;
+        const int2 an = lds.anc[stage][kidx];
+        const int pu = kidx < nk ? an.x : 0x7fffffff;  // keys past the tile: never
 #pragma unroll
-          for (int cg = 0; cg < NCG; ++cg) {
-            const bool vis = (kidx < nk) & (((an.x < ttin[cg]) & (ttin[cg] < an.y)) |
-                                            ((an.x == ttin[cg]) & (u <= trow[cg])));
-            sacc[ks][cg][r] = vis ? sacc[ks][cg][r] : -__builtin_inff();
-          }
+        for (int cg = 0; cg < NCG; ++cg) {
+          const bool vis = (pu <= tpos[cg]) & (tpos[cg] < an.y);
+          sacc[ks][cg][r] = vis ? sacc[ks][cg][r] : -__builtin_inff();
         }
       }
     }
+  };
 
-    float mnew[NCG];
-    bool need_any = false;
+  // Column max of one tile's scores, reduced over the column's four lanes
+  auto tile_max_raw = [&](const f4 (&sacc)[4][NCG], float (&mx)[NCG]) {
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
       float m4[4];
@@ -335,12 +334,12 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
         const f4 x = sacc[ks][cg];
         m4[ks] = max3f(x[0], x[1], fmaxf(x[2], x[3]));
       }
-      const float mx = column_max(max3f(m4[0], m4[1], fmaxf(m4[2], m4[3])));
-      const float ms = mx * scale_log2e;
-      const bool need = ms > mrun[cg] + kRescaleSlack;
-      mnew[cg] = need ? ms : mrun[cg];
-      need_any |= need;
+      mx[cg] = column_max(max3f(m4[0], m4[1], fmaxf(m4[2], m4[3])));
     }
+  };
+
+  // O and the row sums move to the new reference max (rare)
+  auto rescale = [&](bool need_any, const float (&mnew)[NCG]) {
     if (__any(need_any)) {
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
@@ -351,8 +350,11 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
         for (int dt = 0; dt < DT; ++dt) oacc[dt][cg] *= alpha;
       }
     }
+  };
 
-    h8 pb[2][NCG];
+  // P = exp2(s * scale * log2(e) - reference), rounded to f16 in the B-operand
+  // layout of the P.V product
+  auto probs = [&](const f4 (&sacc)[4][NCG], h8 (&pb)[2][NCG]) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -363,41 +365,231 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
           for (int r = 0; r < 4; ++r)
             pb[kc][cg][k2 * 4 + r] = (_Float16)__builtin_amdgcn_exp2f(
                 __builtin_fmaf(sacc[2 * kc + k2][cg][r], scale_log2e, -mrun[cg]));
-    pv_product(s, pb);
+  };
 
-    // the next tile must have landed (only the tile two ahead may still be in
-    // flight) and every wave must be done with this stage before it is reused
-    if (kt + 1 < kte) {
-      if (more) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
-    }
-    __syncthreads();
-    s = s == kStages - 1 ? 0 : s + 1;
-    s2 = s2 == kStages - 1 ? 0 : s2 + 1;
-  }
-
+  // O^T += V^T P^T, row sums += 1^T P^T
+  auto pv_product = [&](int stage, const h8 (&pb)[2][NCG]) {
+    const unsigned char* vl = lds.v[stage];
 #pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) {
-    const float lt = lacc[cg][0];
-    const float inv = 1.0f / lt;
-    if (!cvalid[cg]) continue;
-    const size_t obase = ((size_t)(tile.q_fwd + tok[cg]) * hq + head[cg]) * D;
+    for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const f4 val = oacc[dt][cg] * inv;
-      const int d0 = 16 * dt + 4 * lg;
-      if constexpr (OUT_F32) {
-        *(f4*)((float*)Out + obase + d0) = val;
-      } else {
-        *(h4*)((_Float16*)Out + obase + d0) =
-            h4{(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
+      for (int cg = 0; cg < NCG; ++cg)
+        lacc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[kc][cg], lacc[cg], 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const unsigned char* base = vl + (32 * kc) * ROWB + vbase + 16 * ((2 * dt) ^ vsw);
+        const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(base));
+        const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(base + 16 * ROWB));
+        h8 av;
+        __builtin_memcpy(&av, &lo, 8);
+        __builtin_memcpy((char*)&av + 8, &hi, 8);
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+          oacc[dt][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[kc][cg], oacc[dt][cg], 0, 0, 0);
       }
     }
-    if (Lse != nullptr && lg == 0)
-      Lse[(size_t)head[cg] * n_q_total + tile.q_fwd + tok[cg]] =
-          (mrun[cg] + __log2f(lt)) * 0.69314718055994530942f;
+  };
+
+  // Software pipeline. Step kt runs one hand-ordered block: the scores of
+  // tile kt+1 (K fragments read two sub-steps ahead, NCG MFMAs per fragment)
+  // with the probabilities of tile kt spread between them, then the P.V
+  // product of tile kt (V^T fragments read two sub-steps ahead) with the raw
+  // max of tile kt+1 spread between its MFMAs. Fences keep the compiler from
+  // hoisting every LDS read (which costs registers) or clustering the VALU
+  // work away from the MFMAs. After the block, tile kt+1 is masked if flagged
+  // (its max retaken) and the reference moves (rescaling O, which by then
+  // holds tile kt), so tile kt+1's probabilities need no branch. Tile kt+3's
+  // loads are issued at the start; K(kt+1) and V(kt) are read, so four stages
+  // keep every live tile resident. (Unrolling by two so the two score buffers
+  // swap roles instead of being copied runs out of registers; the copy mostly
+  // coalesces away.)
+  constexpr int NA = 4 * DC;                 // S sub-steps: one K fragment each
+  constexpr int NE = 16 * NCG;               // probabilities per lane per tile
+  constexpr int EPS = (NE + NA - 1) / NA;    // of them per S sub-step
+  constexpr int NB = 2 * DT;                 // P.V sub-steps: one V^T fragment each
+  constexpr int NM = 4 * NCG;                // raw-max partials per lane
+  constexpr int MPS = (NM + NB - 3) / (NB - 2);  // of them per P.V sub-step from the third
+  static_assert(NB > 2 && (NB - 2) * MPS >= NM, "max partials fit");
+
+  auto fused = [&](int sk, int sv, const f4 (&cur)[4][NCG], f4 (&nxt)[4][NCG],
+                   float (&mraw)[NCG]) {
+    const unsigned char* kl = lds.k[sk];
+    const unsigned char* vl = lds.v[sv];
+    h8 kf[NA];
+    s4v vlo[NB], vhi[NB];
+    h8 pb[2][NCG];
+    float mpart[NCG];
+    // sub-step i reads key rows 16*(i / DC) .. +15, head-dim chunk i % DC: one
+    // row block's accumulators complete before the next starts, so the next
+    // tile's scores grow while this tile's are consumed
+    auto kread = [&](int i) {
+      kf[i] = *(const h8*)(kl + (i / DC) * 16 * ROWB + koff[i % DC]);
+    };
+    auto vread = [&](int j) {
+      const unsigned char* base = vl + (32 * (j / DT)) * ROWB + vbase + 16 * ((2 * (j % DT)) ^ vsw);
+      vlo[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(base));
+      vhi[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(base + 16 * ROWB));
+    };
+    // probability e: key chunk kc, column group cg, half k2, element r
+    auto prob = [&](int e) {
+      const int r = e & 3, k2 = (e >> 2) & 1, cg = (e >> 3) % NCG, kc = (e >> 3) / NCG;
+      pb[kc][cg][k2 * 4 + r] = (_Float16)__builtin_amdgcn_exp2f(
+          __builtin_fmaf(cur[2 * kc + k2][cg][r], scale_log2e, -mrun[cg]));
+    };
+    kread(0);
+    if (NA > 1) kread(1);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      if (i + 2 < NA) kread(i + 2);
+      if (i == NA - 2) vread(0);
+      if (i == NA - 1) vread(1);
+#pragma unroll
+      for (int e = i * EPS; e < (i + 1) * EPS && e < NE; ++e) prob(e);
+      const int ks = i / DC, dc = i % DC;
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg)
+        nxt[ks][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            kf[i], qf[cg][dc], dc == 0 ? f4{0.f, 0.f, 0.f, 0.f} : nxt[ks][cg], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (j + 2 < NB) vread(j + 2);
+      const int kc = j / DT, dt = j % DT;
+      if (dt == 0) {
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+          lacc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[kc][cg], lacc[cg], 0, 0, 0);
+      }
+      h8 av;
+      __builtin_memcpy(&av, &vlo[j], 8);
+      __builtin_memcpy((char*)&av + 8, &vhi[j], 8);
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg)
+        oacc[dt][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[kc][cg], oacc[dt][cg], 0, 0, 0);
+      // raw max partials of the next tile's scores (its MFMAs have drained)
+#pragma unroll
+      for (int q = (j - 2) * MPS; q >= 0 && q < (j - 1) * MPS && q < NM; ++q) {
+        const int ks = q % 4, cg = q / 4;
+        const f4 x = nxt[ks][cg];
+        mpart[cg] = ks == 0 ? max3f(x[0], x[1], fmaxf(x[2], x[3]))
+                            : max3f(mpart[cg], max3f(x[0], x[1], x[2]), x[3]);
+      }
+      if (j == NB - 1) {
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) mraw[cg] = column_max(mpart[cg]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // moves the reference to a tile's column max (already reduced over the
+  // column's lanes) when a score exceeds it by kRescaleSlack
+  auto move_reference = [&](const float (&mx)[NCG]) {
+    float mnew[NCG];
+    bool need_any = false;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      const float ms = mx[cg] * scale_log2e;
+      const bool need = ms > mrun[cg] + kRescaleSlack;
+      mnew[cg] = need ? ms : mrun[cg];
+      need_any |= need;
+    }
+    rescale(need_any, mnew);
+  };
+
+  int s = 0;  // stage of the tile being consumed
+  // The end of every consumed tile: the tile two places further on must have
+  // landed (only the one just issued may still be in flight) and every wave
+  // must be done with this tile's stage before it is refilled.
+  auto end_of_tile = [&](bool issued) {
+    if (issued) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
+    __syncthreads();
+    s = (s + 1) & (kStages - 1);
+  };
+  auto step = [&](int kt, const f4 (&cur)[4][NCG], f4 (&nxt)[4][NCG]) {
+    const int s1 = (s + 1) & (kStages - 1);
+    const bool issued = issue_next();
+
+    float mx[NCG];
+    fused(s1, s, cur, nxt, mx);
+
+    const KTile t1 = ktiles[kt + 1];
+    if (t1.meta & kMaskedBit) {
+      apply_mask(s1, t1, nxt);
+      float m[NCG];
+      tile_max_raw(nxt, m);
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) mx[cg] = m[cg];
+    }
+    move_reference(mx);
+    end_of_tile(issued);
+  };
+
+  f4 sa[4][NCG], sb[4][NCG];
+  for (int pos = ib;;) {
+    // ---- item `pos`: Q fragments and columns are loaded -------------------
+    const int ktb = tile.kt_begin, kte = tile.kt_end;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      mrun[cg] = -1e30f;
+      lacc[cg] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt][cg] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+    {
+      s_product(s, sa);
+      const KTile t0 = ktiles[ktb];
+      if (t0.meta & kMaskedBit) apply_mask(s, t0, sa);
+      float mx[NCG];
+      tile_max_raw(sa, mx);
+      move_reference(mx);
+    }
+    for (int kt = ktb; kt + 1 < kte; ++kt) {
+      step(kt, sa, sb);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) sa[ks][cg] = sb[ks][cg];
+    }
+
+    // ---- the item's last tile: its scores are done, so Q is free ----------
+    const bool issued = issue_next();
+    const int o_q_fwd = tile.q_fwd, o_n_tok = tile.n_tok, o_kvh = c_kvh;
+    const bool last = pos + 1 >= ie;
+    if (!last) open_item(pos + 1);
+    {
+      h8 pb[2][NCG];
+      probs(sa, pb);
+      pv_product(s, pb);
+    }
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      const float lt = lacc[cg][0];
+      const float inv = 1.0f / lt;
+      if ((wave * CPW + cg * 16 + l16) / G >= o_n_tok) continue;  // padded column
+      const int o_tok = col_token(cg, o_n_tok), o_head = col_head(cg, o_kvh);
+      const size_t obase = ((size_t)(o_q_fwd + o_tok) * hq + o_head) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f4 val = oacc[dt][cg] * inv;
+        const int d0 = 16 * dt + 4 * lg;
+        if constexpr (OUT_F32) {
+          *(f4*)((float*)Out + obase + d0) = val;
+        } else {
+          *(h4*)((_Float16*)Out + obase + d0) =
+              h4{(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
+        }
+      }
+      if (Lse != nullptr && lg == 0)
+        Lse[(size_t)o_head * n_q_total + o_q_fwd + o_tok] =
+            (mrun[cg] + __log2f(lt)) * 0.69314718055994530942f;
+    }
+    if (last) break;
+    end_of_tile(issued);
+    ++pos;
   }
 }
-
 // Copies this forward's K/V rows into the row-space cache: forward token t
 // goes to cache row tok_rowpos[t]. One thread per 16-byte chunk.
 __global__ void __launch_bounds__(256)
@@ -415,42 +607,57 @@ cache_write_kernel(const _Float16* __restrict__ k_new, const _Float16* __restric
   ((h8*)v_cache)[dst] = ((const h8*)v_new)[src];
 }
 
+// One entry per kernel variant: launch it (a != nullptr) or report how many of
+// its workgroups fit on a compute unit (a == nullptr, result in *per_cu).
 template <int D, int G, int NCG, int WAVES, bool F32>
-static hipError_t launch_variant(const AttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((tree_attn_fwd_kernel<D, G, NCG, WAVES, F32>),
-                     dim3(a.n_work), dim3(WAVES * 64), 0,
-                     st, (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v, a.o,
-                     a.lse, (const QTile*)a.qtiles, (const KTile*)a.ktiles, (const int*)a.work,
-                     (const int2*)a.tok_anc, a.hq, a.hkv, a.n_q, a.scale_log2e);
+static hipError_t variant(const AttnArgs* a, hipStream_t st, int* per_cu) {
+  const auto kernel = tree_attn_fwd_kernel<D, G, NCG, WAVES, F32>;
+  if (!a) return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, kernel, WAVES * 64, 0);
+  hipLaunchKernelGGL(kernel, dim3(a->n_wg), dim3(WAVES * 64), 0, st, (const _Float16*)a->q,
+                     (const _Float16*)a->k, (const _Float16*)a->v, a->o, a->lse,
+                     (const QTile*)a->qtiles, (const KTile*)a->ktiles, (const int*)a->wg_ptr,
+                     (const int*)a->wg_items, (const int2*)a->tok_anc, a->hq, a->hkv, a->n_q,
+                     a->scale_log2e);
   return hipGetLastError();
 }
 
 template <int D, int G>
-static hipError_t launch_group(const AttnArgs& a, hipStream_t st) {
+static hipError_t for_group(bool f32, const AttnArgs* a, hipStream_t st, int* per_cu) {
   constexpr int NCG = column_groups_for(G, D);
   constexpr int WAVES = waves_for(G, D);
-  return a.out_f32 ? launch_variant<D, G, NCG, WAVES, true>(a, st)
-                   : launch_variant<D, G, NCG, WAVES, false>(a, st);
+  return f32 ? variant<D, G, NCG, WAVES, true>(a, st, per_cu)
+             : variant<D, G, NCG, WAVES, false>(a, st, per_cu);
 }
 
 template <int D>
-static hipError_t launch_dim(const AttnArgs& a, hipStream_t st) {
-  switch (a.group) {
-    case 1: return launch_group<D, 1>(a, st);
-    case 2: return launch_group<D, 2>(a, st);
-    case 4: return launch_group<D, 4>(a, st);
-    case 8: return launch_group<D, 8>(a, st);
+static hipError_t for_dim(int group, bool f32, const AttnArgs* a, hipStream_t st, int* per_cu) {
+  switch (group) {
+    case 1: return for_group<D, 1>(f32, a, st, per_cu);
+    case 2: return for_group<D, 2>(f32, a, st, per_cu);
+    case 4: return for_group<D, 4>(f32, a, st, per_cu);
+    case 8: return for_group<D, 8>(f32, a, st, per_cu);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+static hipError_t for_variant(int head_dim, int group, bool f32, const AttnArgs* a, hipStream_t st,
+                              int* per_cu) {
+  switch (head_dim) {
+    case 64: return for_dim<64>(group, f32, a, st, per_cu);
+    case 128: return for_dim<128>(group, f32, a, st, per_cu);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_tree_attention(const AttnArgs& a, hipStream_t st) {
-  if (a.n_work == 0) return hipSuccess;
-  switch (a.head_dim) {
-    case 64: return launch_dim<64>(a, st);
-    case 128: return launch_dim<128>(a, st);
-    default: return hipErrorInvalidValue;
-  }
+  if (a.n_wg == 0) return hipSuccess;
+  return for_variant(a.head_dim, a.group, a.out_f32, &a, st, nullptr);
+}
+
+int attention_blocks_per_cu(int head_dim, int group, bool out_f32) {
+  int per_cu = 0;
+  if (for_variant(head_dim, group, out_f32, nullptr, nullptr, &per_cu) != hipSuccess) return 0;
+  return per_cu;
 }
 
 hipError_t launch_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

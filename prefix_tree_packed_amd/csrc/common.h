@@ -41,13 +41,22 @@ struct ta_plan_s {
   std::vector<ta::QTile> qtiles;
   std::vector<ta::KTile> ktiles;
   std::vector<int32_t> work;        // qtile * num_kv_heads + kv_head, launch order
-  std::vector<ta::Int2> tok_anc;    // per row-space token: (tin, tout) of its block
+  std::vector<ta::Int2> tok_anc;    // per row-space token: (P, subtree end), see number_blocks
   std::vector<int32_t> tok_rowpos;  // per forward token: its row-space index
+  std::vector<double> item_cost;    // per query tile: weighted key tiles (workgroup packing)
   int64_t n_masked_ktiles = 0;
 
   size_t off_qtiles = 0, off_ktiles = 0, off_work = 0, off_anc = 0, off_rowpos = 0;
+  size_t off_wg_ptr = 0, off_wg_items = 0;
   size_t ws_bytes = 0;
   std::vector<unsigned char> image;
 
-  void* d_ws = nullptr;  // workspace of the latest upload
+  int max_workgroups = 0;  // caller's cap on the persistent grid (0: none)
+  int n_wg = 0;            // workgroups of the latest upload
+  void* d_ws = nullptr;    // workspace of the latest upload
 };
+
+namespace ta {
+// Split the work items over n_wg persistent workgroups (see plan.cpp).
+void assign_workgroups(const ta_plan_s* p, int n_wg, int32_t* wg_ptr, int32_t* wg_items);
+}  // namespace ta

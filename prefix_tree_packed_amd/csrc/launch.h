@@ -13,14 +13,18 @@ struct AttnArgs {
   float* lse;
   const void* qtiles;
   const void* ktiles;
-  const void* work;
+  const void* wg_ptr;    // [n_wg + 1] item ranges of the persistent workgroups
+  const void* wg_items;  // work items (query tile * hkv + kv head), per workgroup
   const void* tok_anc;
-  int hq, hkv, head_dim, group, n_q, n_work;
+  int hq, hkv, head_dim, group, n_q, n_wg;
   float scale_log2e;
   bool out_f32;
 };
 
 hipError_t launch_tree_attention(const AttnArgs& a, hipStream_t st);
+// Workgroups of the attention kernel variant for (head_dim, group, out_f32)
+// that fit on one compute unit at once (0 if the variant does not exist).
+int attention_blocks_per_cu(int head_dim, int group, bool out_f32);
 hipError_t launch_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                               const void* tok_rowpos, int n_q, int hkv, int head_dim,
                               hipStream_t st);

@@ -31,6 +31,13 @@ struct KTile {
 
 constexpr int32_t kMaskedBit = 1 << 16;
 
+// Persistent launch: at most this many workgroups, each walking its own list
+// of work items (query tile, KV head).
+constexpr int kMaxWorkgroups = 8192;
+// Number of XCDs (each with its own L2) that consecutive workgroup indices are
+// spread over round-robin on MI355X.
+constexpr int kXcds = 8;
+
 // Kernel variant for a head group size (query heads per KV head) and head
 // dimension: waves per workgroup and 16-column MFMA groups per wave. Columns of
 // a workgroup are (token, head) pairs, head-minor: waves x 16*ncg columns =

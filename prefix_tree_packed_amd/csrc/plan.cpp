@@ -28,6 +28,7 @@
 #include <algorithm>
 #include <new>
 #include <numeric>
+#include <queue>
 #include <string>
 #include <vector>
 
@@ -77,6 +78,7 @@ struct Builder {
   std::vector<int32_t> depth;
   std::vector<int32_t> anc_len;   // summed lengths of proper ancestors
   std::vector<int32_t> tin, tout; // Euler interval of each block over the forest
+  std::vector<int32_t> tpre, tend; // token pre-order start of each block, end of its subtree
   std::vector<uint8_t> has_child;
 
   ta_status validate_and_layout();
@@ -172,10 +174,22 @@ ta_status Builder::validate_and_layout() {
 // blocks in the subtree. Block A is a proper ancestor of B iff
 // tin[A] < tin[B] < tout[A]. Numbers are global, so different rows (and
 // different trees of one row) have disjoint intervals.
+//
+// The same walk numbers tokens: visiting blocks in pre-order and their tokens
+// in order gives token u its pre-order position P(u) = tpre[block] + offset,
+// and tend[block] is the end of the block's subtree in that numbering. Then
+// key u is visible to query t (u's block an ancestor of t's, or the same
+// block with u not after t) iff P(u) <= P(t) < tend[block(u)]: ancestor
+// tokens precede the whole subtree they head, a block's own tokens keep their
+// order, and descendants or unrelated blocks fall after P(t) or at or past
+// the subtree end.
 void Builder::number_blocks() {
   const int32_t NB = (int32_t)start.size();
   tin.assign(NB, 0);
   tout.assign(NB, 0);
+  tpre.assign(NB, 0);
+  tend.assign(NB, 0);
+  int64_t tokens = 0;
   std::vector<std::vector<int32_t>> kids(NB);
   for (int32_t g = 0; g < NB; ++g)
     if (parent[g] >= 0) kids[parent[g]].push_back(g);
@@ -186,14 +200,19 @@ void Builder::number_blocks() {
       if (parent[g] >= 0) continue;
       stack.push_back({g, 0});
       tin[g] = counter++;
+      tpre[g] = (int32_t)tokens;
+      tokens += d->block_len[g];
       while (!stack.empty()) {
         auto& top = stack.back();
         if (top.second < kids[top.first].size()) {
           const int32_t c = kids[top.first][top.second++];
           tin[c] = counter++;
+          tpre[c] = (int32_t)tokens;
+          tokens += d->block_len[c];
           stack.push_back({c, 0});
         } else {
           tout[top.first] = counter;
+          tend[top.first] = (int32_t)tokens;
           stack.pop_back();
         }
       }
@@ -208,7 +227,8 @@ void Builder::token_tables() {
   p->tok_block.resize(nq);
   p->tok_offset.resize(nq);
   p->tok_rowpos.resize(nq);
-  // one key tile of padding: the kernel loads a whole tile's intervals from any k0
+  // one key tile of padding: the kernel loads a whole tile's intervals from any
+  // k0; (0, 0) is visible to no query
   p->tok_anc.assign(p->n_kv + kKeyTile, Int2{0, 0});
   p->useful_pairs = 0;
   p->cost_separate = 0;
@@ -218,7 +238,7 @@ void Builder::token_tables() {
     const RowView& v = rows[r];
     for (int32_t g = v.first_block; g < v.first_block + v.nb; ++g) {
       const int32_t s = start[g], len = d->block_len[g];
-      for (int32_t i = s; i < s + len; ++i) p->tok_anc[v.base + i] = Int2{tin[g], tout[g]};
+      for (int32_t i = s; i < s + len; ++i) p->tok_anc[v.base + i] = Int2{tpre[g] + (i - s), tend[g]};
       const int32_t lo = std::max(s, v.qb), hi = std::min(s + len, v.qe);
       for (int32_t i = lo; i < hi; ++i) {
         const int64_t t = v.q_off + (i - v.qb);
@@ -323,7 +343,8 @@ ta_status Builder::schedule() {
   }
   // longest-first order of query tiles; masked key tiles cost a little more
   const int32_t nqt = (int32_t)p->qtiles.size();
-  std::vector<double> cost(nqt);
+  std::vector<double>& cost = p->item_cost;
+  cost.assign(nqt, 0.0);
   for (int32_t t = 0; t < nqt; ++t) {
     double c = 0;
     for (int32_t k = p->qtiles[t].kt_begin; k < p->qtiles[t].kt_end; ++k)
@@ -362,6 +383,40 @@ static ta_status check_cfg(const ta_attn_cfg* c) {
   return TA_OK;
 }
 
+// Persistent workgroups: longest-processing-time-first packing of the work
+// items (already in longest-first order) into n_wg lists, each item going to
+// the list with the least work so far (ties: lowest index). A workgroup's
+// items cost their weighted key tiles plus about one tile of start-up. When
+// the KV heads and the workgroups both come in multiples of the XCD count,
+// the items of KV head h only go to workgroups w with w = h (mod XCDs): the
+// hardware spreads consecutive workgroups over the XCDs round-robin, so each
+// XCD's L2 then holds the K/V of its own heads only.
+void assign_workgroups(const ta_plan_s* p, int n_wg, int32_t* wg_ptr, int32_t* wg_items) {
+  const int hkv = p->cfg.num_kv_heads;
+  const size_t n = p->work.size();
+  const bool by_xcd = hkv % kXcds == 0 && n_wg % kXcds == 0;
+  const int classes = by_xcd ? kXcds : 1;
+  std::vector<std::vector<int32_t>> lists(n_wg);
+  typedef std::pair<double, int32_t> Load;  // (work so far, workgroup)
+  std::vector<std::priority_queue<Load, std::vector<Load>, std::greater<Load>>> heaps(classes);
+  for (int w = 0; w < n_wg; ++w) heaps[w % classes].push({0.0, w});
+  for (size_t i = 0; i < n; ++i) {
+    const int32_t item = p->work[i];
+    const int c = (item % hkv) % classes;
+    Load l = heaps[c].top();
+    heaps[c].pop();
+    lists[l.second].push_back(item);
+    l.first += 1.0 + p->item_cost[item / hkv];
+    heaps[c].push(l);
+  }
+  int32_t at = 0;
+  for (int w = 0; w < n_wg; ++w) {
+    wg_ptr[w] = at;
+    for (int32_t item : lists[w]) wg_items[at++] = item;
+  }
+  wg_ptr[n_wg] = at;
+}
+
 static void build_image(ta_plan_s* p) {
   size_t off = 0;
   p->off_qtiles = off;
@@ -374,6 +429,11 @@ static void build_image(ta_plan_s* p) {
   off = align256(off + p->tok_anc.size() * sizeof(Int2));
   p->off_rowpos = off;
   off = align256(off + p->tok_rowpos.size() * sizeof(int32_t));
+  // filled by the upload, once the device's workgroup count is known
+  p->off_wg_ptr = off;
+  off = align256(off + (kMaxWorkgroups + 1) * sizeof(int32_t));
+  p->off_wg_items = off;
+  off = align256(off + p->work.size() * sizeof(int32_t));
   p->ws_bytes = std::max<size_t>(off, 256);
   p->image.assign(p->ws_bytes, 0);
   auto put = [&](size_t o, const void* src, size_t n) {
@@ -392,7 +452,9 @@ ta_status build_plan(const ta_tree_desc* desc, const ta_attn_cfg* cfg, ta_plan_s
   p->cfg = *cfg;
   p->group = cfg->num_q_heads / cfg->num_kv_heads;
   p->q_tile_tokens = q_tile_tokens_for(p->group, cfg->head_dim);
-  Builder b{desc, p, {}, {}, {}, {}, {}, {}, {}, {}};
+  Builder b{};
+  b.d = desc;
+  b.p = p;
   if ((st = b.validate_and_layout()) != TA_OK) return st;
   b.number_blocks();
   b.token_tables();
@@ -490,6 +552,26 @@ ta_status tree_attn_plan_schedule(ta_plan_t p, int32_t* q_tiles, int32_t* key_ti
       tok_anc[2 * i] = p->tok_anc[i].x;
       tok_anc[2 * i + 1] = p->tok_anc[i].y;
     }
+  return TA_OK;
+}
+
+ta_status tree_attn_plan_set_max_workgroups(ta_plan_t p, int32_t max_workgroups) {
+  ta::clear_error();
+  if (!p) return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL plan");
+  if (max_workgroups < 0 || max_workgroups > ta::kMaxWorkgroups)
+    return ta::fail(TA_ERR_INVALID_ARGUMENT, "max_workgroups %d outside [0, %d]", max_workgroups,
+                    ta::kMaxWorkgroups);
+  p->max_workgroups = max_workgroups;
+  return TA_OK;
+}
+
+ta_status tree_attn_plan_workgroups(ta_plan_t p, int32_t n_wg, int32_t* wg_ptr, int32_t* wg_items) {
+  ta::clear_error();
+  if (!p || !wg_ptr || (!wg_items && !p->work.empty()))
+    return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (n_wg < 1 || n_wg > ta::kMaxWorkgroups)
+    return ta::fail(TA_ERR_INVALID_ARGUMENT, "n_wg %d outside [1, %d]", n_wg, ta::kMaxWorkgroups);
+  ta::assign_workgroups(p, n_wg, wg_ptr, wg_items);
   return TA_OK;
 }
 

@@ -42,16 +42,18 @@ def _dev(a, dtype=None):
     return t if dtype is None else t.to(dtype)
 
 
-def run_forwards(P, wl, out_dtype="f16", lse=False, forwards=None):
+def run_forwards(P, wl, out_dtype="f16", lse=False, forwards=None, max_workgroups=0):
     """Run a workload's forwards through the C ABI. Chunked workloads share one
     row-space cache across forwards (its prefix before the first forward
-    filled from the generator's K/V: the template computed at start-up)."""
+    filled from the generator's K/V: the template computed at start-up).
+    max_workgroups caps the persistent grid (0: as many as fit the device)."""
     outs, lses, plans = [], [], []
     fwds = wl.forwards if forwards is None else forwards
     cache = None
     for i, f in enumerate(fwds):
         plan = P.tree_attn_plan(f.tree, wl.hq, wl.hkv, wl.d, wl.scale, out_dtype=out_dtype,
                                 write_lse=lse)
+        P.tree_attn_plan_set_max_workgroups(plan, max_workgroups)
         P.tree_attn_plan_upload(plan)
         nq = plan.info["num_q_tokens"]
         q = _dev(f.q)
@@ -166,6 +168,40 @@ def test_deterministic(P):
     a, _, _, _ = run_forwards(P, wl)
     b, _, _, _ = run_forwards(P, wl)
     assert np.array_equal(a[0], b[0])
+
+
+@pytest.mark.parametrize("case", ["doc-questions", "requests", "long-row-chunks", "random-g8",
+                                  "random-g4-d64", "random-g1"])
+def test_persistent_grid_sizes(P, case):
+    """A work item's arithmetic does not depend on the workgroup that runs it,
+    so capping the persistent grid (many items per workgroup, item boundaries
+    inside the K/V load pipeline, one-tile items back to back) changes no bit;
+    the uncapped run matches the oracle."""
+    wl = dict(_small_cases())[case](7)
+    print(f"[persistent] {case}", flush=True)
+    ref, lref, _, _ = run_forwards(P, wl, out_dtype="f32", lse=True)
+    for f, o, l in zip(wl.forwards, ref, lref):
+        want, want_lse = OA.tree_attention(f.tree, f.q, f.k_row, f.v_row, wl.scale, return_lse=True)
+        _compare(o, want)
+        _compare(l, want_lse, atol=LSE_ATOL, rl2=LSE_RL2, what="LSE")
+    for cap in (1, 2, 3, 8, 37):
+        print(f"[persistent] {case} max_workgroups={cap}", flush=True)
+        outs, lses, _, _ = run_forwards(P, wl, out_dtype="f32", lse=True, max_workgroups=cap)
+        for a, b, la, lb in zip(outs, ref, lses, lref):
+            assert np.array_equal(a, b), f"O differs with {cap} workgroups"
+            assert np.array_equal(la, lb), f"LSE differs with {cap} workgroups"
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_persistent_grid_sizes_full(P, cfg):
+    """Full-size workloads with a few hundred items per workgroup give the same
+    bits as the device-sized grid."""
+    wl = W.make_config(cfg, 0)
+    print(f"[persistent] config {cfg}", flush=True)
+    ref, _, _, _ = run_forwards(P, wl)
+    outs, _, _, _ = run_forwards(P, wl, max_workgroups=8)
+    for a, b in zip(outs, ref):
+        assert np.array_equal(a, b)
 
 
 def test_chunked_cache_and_equivalence_with_one_shot(P):

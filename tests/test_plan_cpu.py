@@ -92,12 +92,12 @@ def test_plan_tables_bit_exact(lib, k):
 
 def _expand_schedule(plan, idx, toks):
     """Apply the kernel's rule to the exported schedule: a tile's query tokens
-    see all keys of its unmasked key tiles, and the keys of masked tiles that
-    pass the Euler-interval test. Returns the coverage count per (t, u)."""
+    see all keys of its unmasked key tiles, and the keys u of masked tiles with
+    P(u) <= P(t) < E(u). Returns the coverage count per (t, u)."""
     sch = P.tree_attn_plan_schedule(plan)
     nq, nkv = idx.num_q_tokens, idx.num_kv_tokens
     cover = np.zeros((nq, nkv), np.int16)
-    tin, tout = sch["tok_anc"][:, 0], sch["tok_anc"][:, 1]
+    pre, end = sch["tok_anc"][:, 0], sch["tok_anc"][:, 1]
     seen_q = np.zeros(nq, np.int32)
     for qf, qr, n, kb, ke in sch["q_tiles"]:
         seen_q[qf:qf + n] += 1
@@ -105,15 +105,40 @@ def _expand_schedule(plan, idx, toks):
         for k0, nk, masked in sch["key_tiles"][kb:ke]:
             keys = np.arange(k0, k0 + nk)
             if masked:
-                vis = ((tin[keys][None, :] < tin[trows][:, None]) &
-                       (tin[trows][:, None] < tout[keys][None, :])) | \
-                      ((tin[keys][None, :] == tin[trows][:, None]) &
-                       (keys[None, :] <= trows[:, None]))
+                vis = ((pre[keys][None, :] <= pre[trows][:, None]) &
+                       (pre[trows][:, None] < end[keys][None, :]))
             else:
                 vis = np.ones((n, nk), bool)
             cover[qf:qf + n, k0:k0 + nk] += vis
     assert np.all(seen_q == 1), "every query token in exactly one tile"
     return sch, cover
+
+
+# blocks of a row listed parents-first but not in pre-order (C's subtree sits
+# between B's children), so row order alone cannot decide visibility
+NON_PREORDER = W.desc_from_rows([[(-1, 4), (0, 3), (0, 5), (1, 2), (2, 1), (1, 6)],
+                                 [(-1, 2), (0, 1), (0, 3), (1, 2), (2, 2), (3, 1)]])
+
+
+@pytest.mark.parametrize("k", range(len(DESCS) + 1),
+                         ids=[d[0] for d in DESCS] + ["non-preorder"])
+def test_token_order_encodes_visibility(lib, k):
+    """The exported per-token (P, E) decide visibility for every (query, key)
+    pair, keys outside any schedule included: P(u) <= P(t) < E(u) equals the
+    oracle's ancestor-or-own-prefix mask."""
+    if k < len(DESCS):
+        name, desc, hq, hkv, d = DESCS[k]
+    else:
+        desc, hq, hkv, d = NON_PREORDER, 4, 2, 64
+    idx = OT.build_index(desc)
+    if idx.num_q_tokens * idx.num_kv_tokens > 8192 * 9000:
+        pytest.skip("mask too large for this check")
+    plan = P.tree_attn_plan(desc, hq, hkv, d, d ** -0.5)
+    toks = OT.query_tokens(idx)
+    pre, end = P.tree_attn_plan_schedule(plan)["tok_anc"].T
+    tpos = pre[toks["row_pos"]]
+    enc = (pre[None, :] <= tpos[:, None]) & (tpos[:, None] < end[None, :])
+    np.testing.assert_array_equal(enc, OT.dense_mask(idx, toks))
 
 
 @pytest.mark.parametrize("k", range(len(DESCS)), ids=[d[0] for d in DESCS])
@@ -142,6 +167,46 @@ def test_schedule_covers_mask_exactly_once(lib, k):
     assert costs == sorted(costs, reverse=True)
 
 
+@pytest.mark.parametrize("k", range(len(DESCS)), ids=[d[0] for d in DESCS])
+def test_workgroup_lists(lib, k):
+    """The persistent split covers every work item exactly once, keeps the
+    longest-first order inside each list, is balanced as longest-processing-
+    time packing guarantees (no list exceeds the mean load by more than one
+    item), and keeps each KV head on one XCD class when the counts allow."""
+    name, desc, hq, hkv, d = DESCS[k]
+    plan = P.tree_attn_plan(desc, hq, hkv, d, d ** -0.5)
+    sch = P.tree_attn_plan_schedule(plan)
+    work, qt, kt = sch["work"], sch["q_tiles"], sch["key_tiles"]
+    cost = {}
+    for x in work:
+        kb, ke = qt[x // hkv][3:5]
+        cost[int(x)] = 1.0 + float((1.0 + 0.25 * kt[kb:ke, 2]).sum())
+    rank = {int(x): i for i, x in enumerate(work)}
+    for n_wg in sorted({1, 3, 8, 64, 256, len(work), len(work) + 5}):
+        wg = P.tree_attn_plan_workgroups(plan, n_wg)
+        ptr, items = wg["wg_ptr"], wg["wg_items"]
+        assert ptr[0] == 0 and ptr[-1] == len(work) and np.all(np.diff(ptr) >= 0)
+        assert sorted(items.tolist()) == sorted(work.tolist())
+        loads = []
+        for w in range(n_wg):
+            lst = [int(x) for x in items[ptr[w]:ptr[w + 1]]]
+            assert [rank[x] for x in lst] == sorted(rank[x] for x in lst)
+            loads.append(sum(cost[x] for x in lst))
+            if hkv % 8 == 0 and n_wg % 8 == 0:
+                assert all((x % hkv) % 8 == w % 8 for x in lst)
+        if not (hkv % 8 == 0 and n_wg % 8 == 0):
+            assert max(loads) <= sum(loads) / n_wg + max(cost.values()) + 1e-9
+    # argument checks
+    for bad in (0, -1, 8193):
+        with pytest.raises(P.TreeAttnError):
+            P.tree_attn_plan_workgroups(plan, bad)
+    for bad in (-1, 8193):
+        with pytest.raises(P.TreeAttnError):
+            P.tree_attn_plan_set_max_workgroups(plan, bad)
+    P.tree_attn_plan_set_max_workgroups(plan, 0)
+    P.tree_attn_plan_set_max_workgroups(plan, 8192)
+
+
 def test_long_row_chunks_schedule_rows(lib):
     """For the 32k-token row's chunks check coverage on sampled query tokens."""
     wl = W.make_config(3, 0, tensors=False)
@@ -152,7 +217,7 @@ def test_long_row_chunks_schedule_rows(lib):
         toks = OT.query_tokens(idx)
         plan = P.tree_attn_plan(desc, wl.hq, wl.hkv, wl.d, wl.d ** -0.5)
         sch = P.tree_attn_plan_schedule(plan)
-        tin, tout = sch["tok_anc"][:, 0], sch["tok_anc"][:, 1]
+        pre, end = sch["tok_anc"][:, 0], sch["tok_anc"][:, 1]
         picks = set(rng.integers(0, idx.num_q_tokens, 24).tolist())
         for qf, qr, n, kb, ke in sch["q_tiles"]:
             for t in range(qf, qf + n):
@@ -163,8 +228,7 @@ def test_long_row_chunks_schedule_rows(lib):
                 for k0, nk, masked in sch["key_tiles"][kb:ke]:
                     keys = np.arange(k0, k0 + nk)
                     if masked:
-                        vis = ((tin[keys] < tin[tr]) & (tin[tr] < tout[keys])) | \
-                              ((tin[keys] == tin[tr]) & (keys <= tr))
+                        vis = (pre[keys] <= pre[tr]) & (pre[tr] < end[keys])
                     else:
                         vis = np.ones(nk, bool)
                     row[k0:k0 + nk] += vis
