@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--batch-invariant", action="store_true",
+                    help="key tiles by position in each query's own prompt (bitwise-identical "
+                         "results alone / in a batch / in a tree) instead of the union tiling")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain 256 MiB device copy (known bytes) so "
                          "profiler byte counters can be scaled against it")
@@ -104,7 +107,8 @@ def main():
 
     # ---- plans (host) + device inputs -------------------------------------
     t0 = time.perf_counter()
-    plans = [P.tree_attn_plan(f.tree, wl.hq, wl.hkv, wl.d, wl.scale, out_dtype=args.out_dtype)
+    plans = [P.tree_attn_plan(f.tree, wl.hq, wl.hkv, wl.d, wl.scale, out_dtype=args.out_dtype,
+                              batch_invariant=args.batch_invariant)
              for f in wl.forwards]
     plan_build_ms = (time.perf_counter() - t0) * 1e3
     for p in plans:
@@ -195,6 +199,7 @@ def main():
             "useful_gflop_per_step": round(sum(useful_flops) / 1e9, 3),
             "decisions": d.n_dec,
             "out_dtype": args.out_dtype,
+            "key_tiling": "by prompt position" if args.batch_invariant else "union",
         },
         "roofline": {
             "bound": "mfma",
@@ -210,7 +215,8 @@ def main():
         },
     }
 
-    tr = measured_traffic(args.config, k) if args.seed == 0 and args.out_dtype == "f16" else None
+    tr = (measured_traffic(args.config, k)
+          if args.seed == 0 and args.out_dtype == "f16" and not args.batch_invariant else None)
     if tr is not None:
         out["roofline"]["traffic"] = tr["fetch_bytes"] + tr["write_bytes"]
         out["roofline"]["traffic_detail"] = dict(tr, source=os.path.relpath(TRAFFIC_FILE, ROOT))
@@ -235,10 +241,14 @@ def main():
 def algorithmic_bytes(plan, wl, out_dtype):
     """Q read and O written once, and every K/V row some query sees read once."""
     import prefix_tree_packed_amd as P
-    kt = P.tree_attn_plan_schedule(plan)["key_tiles"]
+    from prefix_tree_packed_amd.binding import key_tile_rows
+    sch = P.tree_attn_plan_schedule(plan)
     seen = np.zeros(plan.info["num_kv_tokens"] + 64, dtype=bool)
-    for k0, n, _ in kt:
-        seen[k0:k0 + n] = True
+    for i, (k0, n, *_rest) in enumerate(sch["key_tiles"]):
+        if _rest[3] == 1:
+            seen[k0:k0 + n] = True
+        else:
+            seen[key_tile_rows(sch, i)] = True
     ob = 2 if out_dtype == "f16" else 4
     q = plan.info["num_q_tokens"] * wl.hq * wl.d
     kv = 2 * int(seen.sum()) * wl.hkv * wl.d * 2

@@ -96,6 +96,15 @@ typedef struct {
  * (grouped heads are contiguous). scale multiplies Q.K before the softmax and
  * must be finite and > 0 (usually 1/sqrt(head_dim)). out_dtype selects the type
  * of O. write_lse != 0 makes the forwards accept an LSE output.
+ * batch_invariant != 0 tiles every query's keys by position in its own prompt
+ * (section 05 "Reproducibility": attention tiled by position; the same result
+ * alone, in a batch and in a tree): key tile j of a query holds the keys at
+ * positions 64j .. 64j+63 of its root-to-leaf prompt, in that order, whatever
+ * else shares the forward, the row, the tree or the query tile, so O and LSE
+ * of a prompt's tokens are bitwise identical alone, in a batch, in a tree, and
+ * one-shot or chunked. 0 (default) tiles the union of the keys a query tile
+ * sees, which packs sibling leaves tighter; results then agree across those
+ * cases only to rounding.
  */
 typedef struct {
   int32_t num_q_heads;
@@ -104,6 +113,7 @@ typedef struct {
   float scale;
   ta_dtype out_dtype;
   int32_t write_lse;
+  int32_t batch_invariant;
 } ta_attn_cfg;
 
 typedef struct {
@@ -118,12 +128,16 @@ typedef struct {
   int32_t num_leaves;      /* leaves whose last token this forward computes               */
   int32_t max_depth;       /* blocks on the longest root-to-leaf path                     */
   int32_t num_q_tiles;     /* query tiles of the block-sparse schedule                    */
-  int32_t num_work_items;  /* query tiles x KV heads: workgroups of one attention launch  */
+  int32_t num_work_items;  /* query tiles x KV heads: work items of one attention launch  */
   int64_t num_key_tiles;   /* key tiles visited summed over query tiles (one KV head)     */
   int64_t num_masked_key_tiles;
   int32_t q_tile_tokens;   /* tokens per query tile                                       */
   int32_t one_shot;        /* 1 if every row is computed whole (tree_attn_forward valid)  */
   size_t workspace_bytes;  /* device workspace tree_attn_plan_upload needs                */
+  int64_t num_segments;    /* entries of the key tiles' segment table (0 unless tiles by
+                              prompt position span several blocks)                        */
+  int32_t batch_invariant; /* the configuration's flag                                    */
+  int32_t pad0;
 } ta_plan_info;
 
 /*
@@ -175,8 +189,11 @@ ta_status tree_attn_plan_export(ta_plan_t plan, int32_t* pos_id, int32_t* tok_ro
  *   q_tiles [num_q_tiles * 5]: per query tile (forward index of its first
  *           token, row-space index of its first token, tokens, first key tile,
  *           end key tile)
- *   key_tiles [num_key_tiles * 3]: per key tile (row-space first key, keys,
- *           1 if the kernel applies the per-key visibility test, else 0)
+ *   key_tiles [num_key_tiles * 7]: per key tile (row-space key of slot 0,
+ *           keys n, 1 if the kernel applies the per-key visibility test else 0,
+ *           lo, hi, segment count, first segment): the tile counts for query t
+ *           only if lo <= P(t) < hi; with one segment slot s holds key
+ *           k0 + s, otherwise segments[first .. first + count) map slots to keys
  *   work [num_work_items]: the work items longest first, each query_tile *
  *           num_kv_heads + kv_head, the KV heads of one tile together
  *   tok_anc [num_kv_tokens * 2]: per row-space token u, (P(u), E(u)): P is
@@ -184,9 +201,13 @@ ta_status tree_attn_plan_export(ta_plan_t plan, int32_t* pos_id, int32_t* tok_ro
  *           and each block's tokens in order, E is the end (exclusive) of
  *           u's block's subtree in that numbering; key u is visible to query
  *           t iff P(u) <= P(t) < E(u)
+ *   segments [num_segments * 2]: (first slot, row-space key of that slot); a
+ *           segment runs to the next one's first slot (the last to n). The
+ *           entry before each tile's first segment is a header the kernel
+ *           uses (where the tile's per-key entries start, slot 0's key)
  */
 ta_status tree_attn_plan_schedule(ta_plan_t plan, int32_t* q_tiles, int32_t* key_tiles,
-                                  int32_t* work, int32_t* tok_anc);
+                                  int32_t* work, int32_t* tok_anc, int32_t* segments);
 
 /*
  * Cap the number of persistent workgroups later uploads may launch (0, the

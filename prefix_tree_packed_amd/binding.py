@@ -49,7 +49,8 @@ class _TreeDesc(ctypes.Structure):
 class _AttnCfg(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("out_dtype", ctypes.c_int), ("write_lse", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int), ("write_lse", ctypes.c_int32),
+                ("batch_invariant", ctypes.c_int32)]
 
 
 class _PlanInfo(ctypes.Structure):
@@ -60,7 +61,9 @@ class _PlanInfo(ctypes.Structure):
                 ("max_depth", ctypes.c_int32), ("num_q_tiles", ctypes.c_int32),
                 ("num_work_items", ctypes.c_int32), ("num_key_tiles", ctypes.c_int64),
                 ("num_masked_key_tiles", ctypes.c_int64), ("q_tile_tokens", ctypes.c_int32),
-                ("one_shot", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+                ("one_shot", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
+                ("num_segments", ctypes.c_int64), ("batch_invariant", ctypes.c_int32),
+                ("pad0", ctypes.c_int32)]
 
 
 _lib = None
@@ -82,7 +85,7 @@ def load_library(path: str = LIB_PATH):
     lib.tree_attn_plan_info.argtypes = [vp, ctypes.POINTER(_PlanInfo)]
     lib.tree_attn_plan_upload.argtypes = [vp, vp, ctypes.c_size_t, vp]
     lib.tree_attn_plan_export.argtypes = [vp, p32, p32, p32, p32, p32, p32]
-    lib.tree_attn_plan_schedule.argtypes = [vp, p32, p32, p32, p32]
+    lib.tree_attn_plan_schedule.argtypes = [vp, p32, p32, p32, p32, p32]
     lib.tree_attn_plan_set_max_workgroups.argtypes = [vp, i32]
     lib.tree_attn_plan_workgroups.argtypes = [vp, i32, p32, p32]
     lib.tree_attn_plan_destroy.argtypes = [vp]
@@ -149,7 +152,8 @@ class Plan:
 
 
 def tree_attn_plan(tree, num_q_heads: int, num_kv_heads: int, head_dim: int, scale: float,
-                   out_dtype: str = "f16", write_lse: bool = False) -> Plan:
+                   out_dtype: str = "f16", write_lse: bool = False,
+                   batch_invariant: bool = False) -> Plan:
     """Build a plan from a tree description (any object with the fields
     row_block_indptr, block_parent, block_len, row_q_begin, row_q_end)."""
     lib = load_library()
@@ -162,13 +166,13 @@ def tree_attn_plan(tree, num_q_heads: int, num_kv_heads: int, head_dim: int, sca
                      _ptr32(qb), _ptr32(qe))
     od = {"f16": TA_F16, "f32": TA_F32}[out_dtype]
     cfg = _AttnCfg(int(num_q_heads), int(num_kv_heads), int(head_dim), float(scale), od,
-                   1 if write_lse else 0)
+                   1 if write_lse else 0, 1 if batch_invariant else 0)
     out = ctypes.c_void_p()
     _check(lib.tree_attn_plan(ctypes.byref(desc), ctypes.byref(cfg), ctypes.byref(out)))
     return Plan(out.value, (indptr, parent, lens, qb, qe),
                 {"num_q_heads": int(num_q_heads), "num_kv_heads": int(num_kv_heads),
                  "head_dim": int(head_dim), "scale": float(scale), "out_dtype": out_dtype,
-                 "write_lse": bool(write_lse)})
+                 "write_lse": bool(write_lse), "batch_invariant": bool(batch_invariant)})
 
 
 def tree_attn_plan_info(plan: Plan) -> dict:
@@ -206,16 +210,31 @@ def tree_attn_plan_export(plan: Plan) -> dict:
 
 
 def tree_attn_plan_schedule(plan: Plan) -> dict:
-    """Host copy of the block-sparse schedule (query tiles, key tiles, work
-    items longest first, per-token pre-order positions and subtree ends)."""
+    """Host copy of the block-sparse schedule (query tiles, key tiles with their
+    visibility interval and segments, work items longest first, per-token
+    pre-order positions and subtree ends)."""
     info = plan.info
     out = {"q_tiles": np.zeros((info["num_q_tiles"], 5), np.int32),
-           "key_tiles": np.zeros((info["num_key_tiles"], 3), np.int32),
+           "key_tiles": np.zeros((info["num_key_tiles"], 7), np.int32),
            "work": np.zeros(info["num_work_items"], np.int32),
-           "tok_anc": np.zeros((info["num_kv_tokens"], 2), np.int32)}
+           "tok_anc": np.zeros((info["num_kv_tokens"], 2), np.int32),
+           "segments": np.zeros((info["num_segments"], 2), np.int32)}
     _check(load_library().tree_attn_plan_schedule(
         plan.handle, _ptr32(out["q_tiles"]), _ptr32(out["key_tiles"]), _ptr32(out["work"]),
-        _ptr32(out["tok_anc"])))
+        _ptr32(out["tok_anc"]), _ptr32(out["segments"])))
+    return out
+
+
+def key_tile_rows(sch: dict, i: int) -> np.ndarray:
+    """Row-space keys of key tile i of an exported schedule, in slot order."""
+    k0, n, _, _, _, nseg, seg = (int(x) for x in sch["key_tiles"][i])
+    if nseg == 1:
+        return np.arange(k0, k0 + n)
+    segs = sch["segments"][seg:seg + nseg]
+    out = np.empty(n, np.int64)
+    for k, (slot0, row0) in enumerate(segs):
+        slot1 = segs[k + 1][0] if k + 1 < nseg else n
+        out[slot0:slot1] = np.arange(row0, row0 + slot1 - slot0)
     return out
 
 

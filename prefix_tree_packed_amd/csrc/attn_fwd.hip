@@ -15,13 +15,15 @@
 // keeps its Q fragments in registers for the whole tile; at head_dim 128 eight
 // waves of two column groups run two per SIMD.
 //
-// Per 64-key tile (three LDS stages; a tile's loads are issued two tiles
-// ahead of its use, straight from global memory into LDS):
+// Per 64-key tile (four LDS stages; a tile's loads are issued three tiles
+// ahead of its P.V product, straight from global memory into LDS):
 //   S^T = K Q^T     v_mfma_f32_16x16x32_f16, A = K rows from LDS, B = Q
 //   mask            only on tiles the plan flags: key u is visible to query t
 //                   iff u's block is a proper ancestor of t's block or the
 //                   same block with u <= t, tested as P(u) <= P(t) < E(u) on
-//                   the plan's token pre-order positions P and subtree ends E
+//                   the plan's token pre-order positions P and subtree ends E,
+//                   and the tile counts for t (its [lo, hi) holds P(t): with
+//                   tiles by prompt position a tile belongs to one path)
 //   softmax         one running reference max per column (two cross-lane steps
 //                   over the 4 lane groups that share a column), moved only
 //                   when a score exceeds it by 2^8; exp2 with log2(e) folded
@@ -147,9 +149,11 @@ __global__ void __launch_bounds__(WAVES * 64)
 tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                         const _Float16* __restrict__ V, void* __restrict__ Out,
                         float* __restrict__ Lse, const QTile* __restrict__ qtiles,
-                        const KTile* __restrict__ ktiles, const int* __restrict__ wg_ptr,
-                        const int* __restrict__ wg_items, const int2* __restrict__ tok_anc, int hq,
-                        int hkv, int n_q_total, float scale_log2e) {
+                        const KTile* __restrict__ ktiles, const int2* __restrict__ kvis,
+                        const Seg* __restrict__ segs,
+                        const int* __restrict__ wg_ptr, const int* __restrict__ wg_items,
+                        const int2* __restrict__ tok_anc, int hq, int hkv, int n_q_total,
+                        float scale_log2e) {
   constexpr int DC = D / 32;
   constexpr int DT = D / 16;
   constexpr int CPW = 16 * NCG;
@@ -179,31 +183,61 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   // land in physical chunk lane%DCH, which holds logical chunk
   // (lane%DCH) ^ (row % DCH) (K) or (lane%DCH) ^ v_swizzle(row) (V).
   const size_t kv_stride = (size_t)hkv * D;
-  int lrow[IPW], kch[IPW], vch[IPW];
+  int lrow[IPW], loff[IPW], kch[IPW], vch[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
     const int row = (wave * IPW + j) * RPI + lane / DCH;
     lrow[j] = row;
+    loff[j] = row * (int)kv_stride;
     kch[j] = 8 * ((lane % DCH) ^ (row % DCH));
     vch[j] = 8 * ((lane % DCH) ^ v_swizzle<DCH>(row));
   }
 
   auto issue = [&](int stage, int kvh, const KTile& t) {
     const int nk = t.meta & 0xffff;
-    const _Float16* kb = K + (size_t)kvh * D + (size_t)t.k0 * kv_stride;
-    const _Float16* vb = V + (size_t)kvh * D + (size_t)t.k0 * kv_stride;
+    const int nseg = ((t.meta >> kSegShift) & (kMaxSegs - 1)) + 1;
+    // slot 0's row and the first per-key (P, E) entry: k0 itself for a
+    // one-segment tile, else from the header at segs[k0]
+    int k0 = t.k0, anc = t.k0;
+    if (nseg > 1) {
+      const Seg h = segs[t.k0];
+      anc = h.slot0;
+      k0 = h.row0;
+    }
+    const _Float16* kb = K + (size_t)kvh * D + (size_t)k0 * kv_stride;
+    const _Float16* vb = V + (size_t)kvh * D + (size_t)k0 * kv_stride;
+    // element offset of each loaded slot's row from slot 0's row: the slot
+    // itself for a one-segment tile (precomputed), else from the segment
+    // holding it (later segments are descendant blocks, laid out after slot
+    // 0's block in the row). Slots past the tile's keys re-read slot 0's row
+    // (finite data; such slots only occur in flagged tiles, where they get
+    // -inf scores).
+    int roff[IPW];
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) roff[j] = lrow[j] < nk ? loff[j] : 0;
+    if (nseg > 1) {
+      const Seg* sg = segs + t.k0 + 1;  // sg[0] starts at slot 0, row k0
+      int rel[IPW];
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) rel[j] = lrow[j];
+      for (int k = 1; k < nseg; ++k) {
+        const Seg x = sg[k];
+#pragma unroll
+        for (int j = 0; j < IPW; ++j)
+          rel[j] = lrow[j] >= x.slot0 ? x.row0 - k0 + (lrow[j] - x.slot0) : rel[j];
+      }
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) roff[j] = lrow[j] < nk ? rel[j] * (int)kv_stride : 0;
+    }
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
-      // rows past the tile's keys re-read the tile's first row (finite data;
-      // such rows only occur in flagged tiles, where they get -inf scores)
-      const int roff = lrow[j] < nk ? lrow[j] * (int)kv_stride : 0;
-      lds_dma16(kb + roff + kch[j], lds_addr_of(lds.k[stage] + (wave * IPW + j) * 1024));
-      lds_dma16(vb + roff + vch[j], lds_addr_of(lds.v[stage] + (wave * IPW + j) * 1024));
+      lds_dma16(kb + roff[j] + kch[j], lds_addr_of(lds.k[stage] + (wave * IPW + j) * 1024));
+      lds_dma16(vb + roff[j] + vch[j], lds_addr_of(lds.v[stage] + (wave * IPW + j) * 1024));
     }
-    // (P, E) of the tile's keys (ANCB bytes per wave; the plan pads tok_anc so
-    // a full tile's worth past any k0 is readable)
+    // (P, E) of the tile's 64 slots (ANCB bytes per wave; the plan pads
+    // tok_anc so a full tile's worth past any entry is readable)
     if (lane < ANCB / 16)
-      lds_dma16((const char*)(tok_anc + t.k0) + wave * ANCB + 16 * lane,
+      lds_dma16((const char*)(tok_anc + anc) + wave * ANCB + 16 * lane,
                 lds_addr_of((const char*)lds.anc[stage] + wave * ANCB));
   };
 
@@ -305,19 +339,25 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     }
   };
 
-  // -inf for keys query t must not see (flagged tiles only)
-  auto apply_mask = [&](int stage, const KTile& t, f4 (&sacc)[4][NCG]) {
+  // -inf for keys query t must not see (flagged tiles only): the tile must
+  // count for t (lo <= P(t) < hi; else t's position is taken as -1, which no
+  // key passes) and key u must pass P(u) <= P(t) < E(u)
+  auto apply_mask = [&](int stage, int kt, const KTile& t, f4 (&sacc)[4][NCG]) {
     const int nk = t.meta & 0xffff;
+    const int2 vis = kvis[kt];
+    int tp[NCG];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) tp[cg] = ((vis.x <= tpos[cg]) & (tpos[cg] < vis.y)) ? tpos[cg] : -1;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kidx = 16 * ks + 4 * lg + r;
         const int2 an = lds.anc[stage][kidx];
-        const int pu = kidx < nk ? an.x : 0x7fffffff;  // keys past the tile: never
+        const int pu = kidx < nk ? an.x : 0x7fffffff;  // slots past the tile: never
 #pragma unroll
         for (int cg = 0; cg < NCG; ++cg) {
-          const bool vis = (pu <= tpos[cg]) & (tpos[cg] < an.y);
+          const bool vis = (pu <= tp[cg]) & (tp[cg] < an.y);
           sacc[ks][cg][r] = vis ? sacc[ks][cg][r] : -__builtin_inff();
         }
       }
@@ -516,7 +556,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
 
     const KTile t1 = ktiles[kt + 1];
     if (t1.meta & kMaskedBit) {
-      apply_mask(s1, t1, nxt);
+      apply_mask(s1, kt + 1, t1, nxt);
       float m[NCG];
       tile_max_raw(nxt, m);
 #pragma unroll
@@ -540,7 +580,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     {
       s_product(s, sa);
       const KTile t0 = ktiles[ktb];
-      if (t0.meta & kMaskedBit) apply_mask(s, t0, sa);
+      if (t0.meta & kMaskedBit) apply_mask(s, ktb, t0, sa);
       float mx[NCG];
       tile_max_raw(sa, mx);
       move_reference(mx);
@@ -615,7 +655,9 @@ static hipError_t variant(const AttnArgs* a, hipStream_t st, int* per_cu) {
   if (!a) return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, kernel, WAVES * 64, 0);
   hipLaunchKernelGGL(kernel, dim3(a->n_wg), dim3(WAVES * 64), 0, st, (const _Float16*)a->q,
                      (const _Float16*)a->k, (const _Float16*)a->v, a->o, a->lse,
-                     (const QTile*)a->qtiles, (const KTile*)a->ktiles, (const int*)a->wg_ptr,
+                     (const QTile*)a->qtiles, (const KTile*)a->ktiles, (const int2*)a->kvis,
+                     (const Seg*)a->segs,
+                     (const int*)a->wg_ptr,
                      (const int*)a->wg_items, (const int2*)a->tok_anc, a->hq, a->hkv, a->n_q,
                      a->scale_log2e);
   return hipGetLastError();

@@ -40,13 +40,17 @@ struct ta_plan_s {
   // device tables, laid out in `image` at the offsets below (256-byte aligned)
   std::vector<ta::QTile> qtiles;
   std::vector<ta::KTile> ktiles;
+  std::vector<ta::Int2> kvis;       // per key tile: [lo, hi) of the queries it counts for
+  std::vector<ta::Seg> segs;        // header + segments of each multi-segment key tile
   std::vector<int32_t> work;        // qtile * num_kv_heads + kv_head, launch order
-  std::vector<ta::Int2> tok_anc;    // per row-space token: (P, subtree end), see number_blocks
+  std::vector<ta::Int2> tok_anc;    // per row-space token: (P, subtree end), see number_blocks;
+                                    // then 64 entries per multi-segment key tile
   std::vector<int32_t> tok_rowpos;  // per forward token: its row-space index
   std::vector<double> item_cost;    // per query tile: weighted key tiles (workgroup packing)
   int64_t n_masked_ktiles = 0;
 
-  size_t off_qtiles = 0, off_ktiles = 0, off_work = 0, off_anc = 0, off_rowpos = 0;
+  size_t off_qtiles = 0, off_ktiles = 0, off_kvis = 0, off_segs = 0, off_work = 0, off_anc = 0,
+         off_rowpos = 0;
   size_t off_wg_ptr = 0, off_wg_items = 0;
   size_t ws_bytes = 0;
   std::vector<unsigned char> image;

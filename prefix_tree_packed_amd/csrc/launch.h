@@ -13,6 +13,8 @@ struct AttnArgs {
   float* lse;
   const void* qtiles;
   const void* ktiles;
+  const void* kvis;      // per key tile: [lo, hi) of the queries it counts for
+  const void* segs;      // headers and segments of multi-segment key tiles
   const void* wg_ptr;    // [n_wg + 1] item ranges of the persistent workgroups
   const void* wg_items;  // work items (query tile * hkv + kv head), per workgroup
   const void* tok_anc;

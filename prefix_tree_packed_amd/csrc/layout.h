@@ -20,16 +20,32 @@ struct QTile {
   int32_t pad0, pad1, pad2;
 };
 
-// One key tile: keys [k0, k0 + n) in row space, n <= kKeyTile. `meta` holds n
-// in its low 16 bits and, in bit 16, whether the tile needs the per-element
-// visibility test (some key is not visible to every query of the tile, or the
-// tile is short).
+// One key tile: n <= kKeyTile keys in slots [0, n). `meta` holds n in its low
+// 16 bits, in bit 16 whether the tile needs the per-element visibility test
+// (some key is not visible to every query of the tile, or the tile is short),
+// and nseg - 1 in bits 17-19. With one segment, slot s holds row-space key
+// k0 + s and the per-key (P, E) entries start at tok_anc[k0]. With several,
+// k0 is an index h into the segment table: segs[h] = {first (P, E) entry, row
+// of slot 0} and segs[h + 1 .. h + nseg] are the segments (Seg below). Kept at
+// 8 bytes so a scalar-cache line holds 8 tiles; the tile's visibility interval
+// lives in a side table read only for flagged tiles: the tile counts for query
+// t only if lo <= P(t) < hi (P: the token pre-order position).
 struct KTile {
   int32_t k0;
   int32_t meta;
 };
 
+// Segment of a multi-segment key tile: slots [slot0, next segment's slot0)
+// hold row-space keys row0, row0 + 1, ... (also the header layout, see KTile)
+struct Seg {
+  int32_t slot0;
+  int32_t row0;
+};
+
 constexpr int32_t kMaskedBit = 1 << 16;
+constexpr int kSegShift = 17;
+// A key tile lies on one root-to-leaf path, which has at most this many blocks.
+constexpr int kMaxSegs = 8;
 
 // Persistent launch: at most this many workgroups, each walking its own list
 // of work items (query tile, KV head).

@@ -85,6 +85,7 @@ struct Builder {
   void number_blocks();
   void token_tables();
   ta_status schedule();
+  void position_tiles(const RowView& v, int32_t a, int32_t b);
   int32_t block_of(const RowView& r, int32_t i) const;
   bool chunk_full(const RowView& r, int32_t k0, int32_t k1, int32_t a,
                   const std::vector<int32_t>& touched) const;
@@ -290,17 +291,133 @@ bool Builder::chunk_full(const RowView& r, int32_t k0, int32_t k1, int32_t a,
   return true;
 }
 
+// Key tiles of one query tile (row-local tokens [a, b) of row v) by position in
+// each query's own prompt: for every block B the tile touches and every window
+// j = 0 .. (largest position of B's tokens here) / 64, the window holds the
+// keys at prompt positions [64j, 64j + 64) of B's root-to-leaf path. Its
+// owner is the path block holding the window's last position, or B when the
+// path ends inside the window; windows are shared across the tile's blocks by
+// (j, owner), since the prompts of the owner's subtree agree on them. Full
+// windows count for queries in the owner's subtree, cut ones only for queries
+// in the owner itself. The window's keys lie in at most kMaxSegs blocks (the
+// depth limit), each a contiguous row range: one segment per block.
+void Builder::position_tiles(const RowView& v, int32_t a, int32_t b) {
+  struct Win {
+    int32_t j, owner, n;
+    bool full;
+    int32_t path[kMaxSegs];
+    int32_t path_len;
+  };
+  std::vector<Win> wins;
+  const int32_t B0 = block_of(v, a), B1 = block_of(v, b - 1);
+  for (int32_t B = B0; B <= B1; ++B) {
+    int32_t path[kMaxSegs], len = 0;
+    for (int32_t A = B; A >= 0; A = parent[A]) path[len++] = A;
+    std::reverse(path, path + len);
+    const int32_t last_tok = std::min(b, start[B] + d->block_len[B]) - 1;
+    const int32_t max_pos = anc_len[B] + (last_tok - start[B]);
+    const int32_t end_b = anc_len[B] + d->block_len[B];
+    for (int32_t j = 0; j <= max_pos / kKeyTile; ++j) {
+      const int32_t w0 = j * kKeyTile, w1 = w0 + kKeyTile;
+      Win w;
+      w.j = j;
+      w.full = end_b >= w1;
+      if (w.full) {
+        int32_t k = 0;
+        while (anc_len[path[k]] + d->block_len[path[k]] < w1) ++k;
+        w.owner = path[k];
+        w.n = kKeyTile;
+      } else {
+        w.owner = B;
+        w.n = end_b - w0;
+      }
+      bool seen = false;
+      for (const Win& x : wins) seen |= (x.j == j && x.owner == w.owner);
+      if (seen) continue;
+      w.path_len = len;
+      std::copy(path, path + len, w.path);
+      wins.push_back(w);
+    }
+  }
+  std::sort(wins.begin(), wins.end(), [&](const Win& x, const Win& y) {
+    return x.j != y.j ? x.j < y.j : tin[x.owner] < tin[y.owner];
+  });
+  for (const Win& w : wins) {
+    const int32_t w0 = w.j * kKeyTile;
+    KTile kt{};
+    Int2 vis;
+    vis.x = tpre[w.owner];
+    vis.y = w.full ? tend[w.owner] : tpre[w.owner] + d->block_len[w.owner];
+    // segments: the path blocks overlapping positions [w0, w0 + n)
+    Seg sg[kMaxSegs];
+    int nseg = 0;
+    for (int32_t k = 0; k < w.path_len; ++k) {
+      const int32_t A = w.path[k];
+      const int32_t p0 = std::max(anc_len[A], w0), p1 = std::min(anc_len[A] + d->block_len[A], w0 + w.n);
+      if (p0 >= p1) continue;
+      sg[nseg].slot0 = p0 - w0;
+      sg[nseg].row0 = (int32_t)(v.base + start[A] + (p0 - anc_len[A]));
+      ++nseg;
+    }
+    // every query of the tile sees every key of a full window it owns a
+    // position past: then the per-key test can be skipped
+    bool all = w.n == kKeyTile;
+    for (int32_t i = a; i < b && all; ++i) {
+      const int32_t B = block_of(v, i);
+      const int32_t pt = tpre[B] + (i - start[B]);
+      const int32_t pos = anc_len[B] + (i - start[B]);
+      all = vis.x <= pt && pt < vis.y && pos >= w0 + kKeyTile - 1;
+    }
+    kt.meta = w.n | (all ? 0 : kMaskedBit) | ((nseg - 1) << kSegShift);
+    if (nseg == 1) {
+      kt.k0 = sg[0].row0;
+    } else {
+      kt.k0 = (int32_t)p->segs.size();
+      p->segs.push_back(Seg{(int32_t)p->tok_anc.size(), sg[0].row0});  // header
+      for (int k = 0; k < nseg; ++k) p->segs.push_back(sg[k]);
+      for (int32_t slot = 0; slot < kKeyTile; ++slot) {
+        Int2 e{0, 0};
+        for (int k = nseg - 1; k >= 0; --k)
+          if (slot < w.n && slot >= sg[k].slot0) {
+            e = p->tok_anc[sg[k].row0 + (slot - sg[k].slot0)];
+            break;
+          }
+        p->tok_anc.push_back(e);
+      }
+    }
+    if (!all) ++p->n_masked_ktiles;
+    p->ktiles.push_back(kt);
+    p->kvis.push_back(vis);
+  }
+}
+
 ta_status Builder::schedule() {
   const int TQ = p->q_tile_tokens;
   const int hkv = p->cfg.num_kv_heads;
   p->qtiles.clear();
   p->ktiles.clear();
+  p->kvis.clear();
+  p->segs.clear();
   p->n_masked_ktiles = 0;
   std::vector<std::pair<int32_t, int32_t>> ranges;
   std::vector<int32_t> touched;
   for (const RowView& v : rows) {
     for (int32_t a = v.qb; a < v.qe; a += TQ) {
       const int32_t b = std::min(a + TQ, v.qe);
+      if (p->cfg.batch_invariant) {
+        QTile qt{};
+        qt.q_fwd = (int32_t)(v.q_off + (a - v.qb));
+        qt.q_row = (int32_t)(v.base + a);
+        qt.n_tok = b - a;
+        qt.kt_begin = (int32_t)p->ktiles.size();
+        position_tiles(v, a, b);
+        qt.kt_end = (int32_t)p->ktiles.size();
+        if ((int64_t)p->ktiles.size() > (int64_t)INT32_MAX / 2 ||
+            (int64_t)p->tok_anc.size() > (int64_t)INT32_MAX / 2)
+          return fail(TA_ERR_LIMIT, "schedule too large");
+        p->qtiles.push_back(qt);
+        continue;
+      }
       const int32_t B0 = block_of(v, a), B1 = block_of(v, b - 1);
       touched.clear();
       ranges.clear();
@@ -327,10 +444,11 @@ ta_status Builder::schedule() {
         for (int32_t k0 = s; k0 < e; k0 += kKeyTile) {
           const int32_t k1 = std::min(k0 + kKeyTile, e);
           const bool full = (k1 - k0 == kKeyTile) && chunk_full(v, k0, k1, a, touched);
-          KTile kt;
+          KTile kt{};
           kt.k0 = (int32_t)(v.base + k0);
           kt.meta = (k1 - k0) | (full ? 0 : kMaskedBit);
           p->ktiles.push_back(kt);
+          p->kvis.push_back(Int2{0, INT32_MAX});
           if (!full) ++p->n_masked_ktiles;
         }
         i = j;
@@ -423,6 +541,10 @@ static void build_image(ta_plan_s* p) {
   off = align256(off + p->qtiles.size() * sizeof(QTile));
   p->off_ktiles = off;
   off = align256(off + p->ktiles.size() * sizeof(KTile));
+  p->off_kvis = off;
+  off = align256(off + p->kvis.size() * sizeof(Int2));
+  p->off_segs = off;
+  off = align256(off + p->segs.size() * sizeof(Seg));
   p->off_work = off;
   off = align256(off + p->work.size() * sizeof(int32_t));
   p->off_anc = off;
@@ -441,6 +563,8 @@ static void build_image(ta_plan_s* p) {
   };
   put(p->off_qtiles, p->qtiles.data(), p->qtiles.size() * sizeof(QTile));
   put(p->off_ktiles, p->ktiles.data(), p->ktiles.size() * sizeof(KTile));
+  put(p->off_kvis, p->kvis.data(), p->kvis.size() * sizeof(Int2));
+  put(p->off_segs, p->segs.data(), p->segs.size() * sizeof(Seg));
   put(p->off_work, p->work.data(), p->work.size() * sizeof(int32_t));
   put(p->off_anc, p->tok_anc.data(), p->tok_anc.size() * sizeof(Int2));
   put(p->off_rowpos, p->tok_rowpos.data(), p->tok_rowpos.size() * sizeof(int32_t));
@@ -507,6 +631,8 @@ ta_status tree_attn_plan_info(ta_plan_t p, ta_plan_info* out) {
   out->q_tile_tokens = p->q_tile_tokens;
   out->one_shot = p->one_shot;
   out->workspace_bytes = p->ws_bytes;
+  out->num_segments = (int64_t)p->segs.size();
+  out->batch_invariant = p->cfg.batch_invariant ? 1 : 0;
   return TA_OK;
 }
 
@@ -527,7 +653,7 @@ ta_status tree_attn_plan_export(ta_plan_t p, int32_t* pos_id, int32_t* tok_row, 
 }
 
 ta_status tree_attn_plan_schedule(ta_plan_t p, int32_t* q_tiles, int32_t* key_tiles, int32_t* work,
-                                  int32_t* tok_anc) {
+                                  int32_t* tok_anc, int32_t* segments) {
   ta::clear_error();
   if (!p) return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL plan");
   if (q_tiles)
@@ -542,9 +668,21 @@ ta_status tree_attn_plan_schedule(ta_plan_t p, int32_t* q_tiles, int32_t* key_ti
     }
   if (key_tiles)
     for (size_t i = 0; i < p->ktiles.size(); ++i) {
-      key_tiles[3 * i] = p->ktiles[i].k0;
-      key_tiles[3 * i + 1] = p->ktiles[i].meta & 0xffff;
-      key_tiles[3 * i + 2] = (p->ktiles[i].meta & ta::kMaskedBit) ? 1 : 0;
+      const ta::KTile& t = p->ktiles[i];
+      const int nseg = ((t.meta >> ta::kSegShift) & (ta::kMaxSegs - 1)) + 1;
+      int32_t* o = key_tiles + 7 * i;
+      o[0] = nseg == 1 ? t.k0 : p->segs[t.k0].row0;
+      o[1] = t.meta & 0xffff;
+      o[2] = (t.meta & ta::kMaskedBit) ? 1 : 0;
+      o[3] = p->kvis[i].x;
+      o[4] = p->kvis[i].y;
+      o[5] = nseg;
+      o[6] = nseg == 1 ? -1 : t.k0 + 1;
+    }
+  if (segments)
+    for (size_t i = 0; i < p->segs.size(); ++i) {
+      segments[2 * i] = p->segs[i].slot0;
+      segments[2 * i + 1] = p->segs[i].row0;
     }
   if (work && !p->work.empty()) memcpy(work, p->work.data(), p->work.size() * sizeof(int32_t));
   if (tok_anc)

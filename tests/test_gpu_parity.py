@@ -42,7 +42,8 @@ def _dev(a, dtype=None):
     return t if dtype is None else t.to(dtype)
 
 
-def run_forwards(P, wl, out_dtype="f16", lse=False, forwards=None, max_workgroups=0):
+def run_forwards(P, wl, out_dtype="f16", lse=False, forwards=None, max_workgroups=0,
+                 batch_invariant=False):
     """Run a workload's forwards through the C ABI. Chunked workloads share one
     row-space cache across forwards (its prefix before the first forward
     filled from the generator's K/V: the template computed at start-up).
@@ -52,7 +53,7 @@ def run_forwards(P, wl, out_dtype="f16", lse=False, forwards=None, max_workgroup
     cache = None
     for i, f in enumerate(fwds):
         plan = P.tree_attn_plan(f.tree, wl.hq, wl.hkv, wl.d, wl.scale, out_dtype=out_dtype,
-                                write_lse=lse)
+                                write_lse=lse, batch_invariant=batch_invariant)
         P.tree_attn_plan_set_max_workgroups(plan, max_workgroups)
         P.tree_attn_plan_upload(plan)
         nq = plan.info["num_q_tokens"]
@@ -110,6 +111,21 @@ def test_small_parity(P, case, seed, out_dtype):
     wl = make(seed)
     print(f"[parity] {name} seed={seed} out={out_dtype}", flush=True)
     outs, lses, _, _ = run_forwards(P, wl, out_dtype=out_dtype, lse=True)
+    for f, o, l in zip(wl.forwards, outs, lses):
+        want, want_lse = OA.tree_attention(f.tree, f.q, f.k_row, f.v_row, wl.scale, return_lse=True)
+        _compare(o, want)
+        _compare(l, want_lse, atol=LSE_ATOL, rl2=LSE_RL2, what="LSE")
+
+
+@pytest.mark.parametrize("case", range(len(_small_cases())), ids=[c[0] for c in _small_cases()])
+@pytest.mark.parametrize("cap", [0, 5])
+def test_small_parity_tiles_by_position(P, case, cap):
+    """The same parity bar with key tiles by prompt position (batch_invariant),
+    device-sized grid and a 5-workgroup grid."""
+    name, make = _small_cases()[case]
+    wl = make(1)
+    print(f"[parity by position] {name} cap={cap}", flush=True)
+    outs, lses, _, _ = run_forwards(P, wl, lse=True, max_workgroups=cap, batch_invariant=True)
     for f, o, l in zip(wl.forwards, outs, lses):
         want, want_lse = OA.tree_attention(f.tree, f.q, f.k_row, f.v_row, wl.scale, return_lse=True)
         _compare(o, want)

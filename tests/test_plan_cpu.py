@@ -14,6 +14,7 @@ from workloads import configs as W
 
 P = pytest.importorskip("prefix_tree_packed_amd")
 from prefix_tree_packed_amd import binding as B  # noqa: E402
+from prefix_tree_packed_amd.binding import key_tile_rows  # noqa: E402
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -92,8 +93,9 @@ def test_plan_tables_bit_exact(lib, k):
 
 def _expand_schedule(plan, idx, toks):
     """Apply the kernel's rule to the exported schedule: a tile's query tokens
-    see all keys of its unmasked key tiles, and the keys u of masked tiles with
-    P(u) <= P(t) < E(u). Returns the coverage count per (t, u)."""
+    see all keys of its unmasked key tiles, and the keys u of masked tiles that
+    count for t (lo <= P(t) < hi) with P(u) <= P(t) < E(u). Returns the
+    coverage count per (t, u)."""
     sch = P.tree_attn_plan_schedule(plan)
     nq, nkv = idx.num_q_tokens, idx.num_kv_tokens
     cover = np.zeros((nq, nkv), np.int16)
@@ -102,14 +104,17 @@ def _expand_schedule(plan, idx, toks):
     for qf, qr, n, kb, ke in sch["q_tiles"]:
         seen_q[qf:qf + n] += 1
         trows = np.arange(qr, qr + n)
-        for k0, nk, masked in sch["key_tiles"][kb:ke]:
-            keys = np.arange(k0, k0 + nk)
+        for i in range(kb, ke):
+            _, nk, masked, lo, hi, _, _ = sch["key_tiles"][i]
+            keys = key_tile_rows(sch, i)
+            assert len(keys) == nk
             if masked:
-                vis = ((pre[keys][None, :] <= pre[trows][:, None]) &
-                       (pre[trows][:, None] < end[keys][None, :]))
+                pt = pre[trows]
+                vis = ((lo <= pt) & (pt < hi))[:, None] & (pre[keys][None, :] <= pt[:, None]) & \
+                      (pt[:, None] < end[keys][None, :])
             else:
                 vis = np.ones((n, nk), bool)
-            cover[qf:qf + n, k0:k0 + nk] += vis
+            np.add.at(cover, (slice(qf, qf + n), keys), vis)
     assert np.all(seen_q == 1), "every query token in exactly one tile"
     return sch, cover
 
@@ -141,13 +146,14 @@ def test_token_order_encodes_visibility(lib, k):
     np.testing.assert_array_equal(enc, OT.dense_mask(idx, toks))
 
 
+@pytest.mark.parametrize("inv", [False, True], ids=["union", "by-position"])
 @pytest.mark.parametrize("k", range(len(DESCS)), ids=[d[0] for d in DESCS])
-def test_schedule_covers_mask_exactly_once(lib, k):
+def test_schedule_covers_mask_exactly_once(lib, k, inv):
     name, desc, hq, hkv, d = DESCS[k]
     idx = OT.build_index(desc)
     if idx.num_q_tokens * idx.num_kv_tokens > 8192 * 9000:
         pytest.skip("mask too large for this check")  # the long-row chunks
-    plan = P.tree_attn_plan(desc, hq, hkv, d, d ** -0.5)
+    plan = P.tree_attn_plan(desc, hq, hkv, d, d ** -0.5, batch_invariant=inv)
     toks = OT.query_tokens(idx)
     sch, cover = _expand_schedule(plan, idx, toks)
     mask = OT.dense_mask(idx, toks)
@@ -165,6 +171,64 @@ def test_schedule_covers_mask_exactly_once(lib, k):
         kb, ke = sch["q_tiles"][x // hkv][3:5]
         costs.append(float((1.0 + 0.25 * kt[kb:ke, 2]).sum()))  # masked tiles weigh 1.25
     assert costs == sorted(costs, reverse=True)
+
+
+@pytest.mark.parametrize("k", range(len(DESCS) + 1), ids=[d[0] for d in DESCS] + ["non-preorder"])
+def test_tiles_by_prompt_position(lib, k):
+    """With batch_invariant the key tiles a query token counts form the same
+    sequence whatever shares its forward, row, tree or query tile: tile j holds
+    the keys at positions 64j .. 64j+63 of the token's own prompt in that order
+    (slot s = position - 64j), one tile per j for j = 0 .. pos // 64, in
+    increasing j, and every other tile of its query tile is fully masked for it
+    (a fully masked tile adds exact zeros and leaves the running max alone).
+    This is what makes the kernel's result depend on the prompt only."""
+    if k < len(DESCS):
+        name, desc, hq, hkv, d = DESCS[k]
+    else:
+        desc, hq, hkv, d = NON_PREORDER, 4, 2, 64
+    idx = OT.build_index(desc)
+    plan = P.tree_attn_plan(desc, hq, hkv, d, d ** -0.5, batch_invariant=True)
+    assert plan.info["batch_invariant"] == 1
+    sch = P.tree_attn_plan_schedule(plan)
+    toks = OT.query_tokens(idx)
+    pre, end = sch["tok_anc"][:, 0], sch["tok_anc"][:, 1]
+    # prompt position of every row-space key on the path of each block
+    nkv = idx.num_kv_tokens
+    key_block = np.zeros(nkv, np.int64)
+    for g in range(len(idx.block_len)):
+        b0 = idx.row_base[idx.block_row[g]] + idx.block_start[g]
+        key_block[b0:b0 + idx.block_len[g]] = g
+    anc_len = [sum(idx.block_len[a] for a in idx.block_anc[g]) for g in range(len(idx.block_len))]
+    rng = np.random.default_rng(k)
+    sample = set(rng.choice(idx.num_q_tokens, min(idx.num_q_tokens, 300), replace=False).tolist())
+    for qf, qr, n, kb, ke in sch["q_tiles"]:
+        for t in range(qf, qf + n):
+            if t not in sample:
+                continue
+            tr = qr + (t - qf)
+            blk, pos = int(toks["tok_block"][t]), int(toks["pos_id"][t])
+            path = set(idx.block_anc[blk]) | {blk}
+            js = []
+            for i in range(kb, ke):
+                _, nk, masked, lo, hi, _, _ = sch["key_tiles"][i]
+                keys = key_tile_rows(sch, i)
+                counts = not masked or lo <= pre[tr] < hi
+                vis = np.ones(nk, bool) if not masked else \
+                    (lo <= pre[tr] < hi) & (pre[keys] <= pre[tr]) & (pre[tr] < end[keys])
+                if not counts:
+                    assert not vis.any()
+                    continue
+                # a counted tile lies on the token's path at positions 64j + slot
+                kbk = key_block[keys]
+                assert all(int(g) in path for g in kbk)
+                kpos = np.array([anc_len[int(g)] for g in kbk]) + \
+                    (keys - np.array([idx.row_base[idx.block_row[int(g)]] + idx.block_start[int(g)] for g in kbk]))
+                j = int(kpos[0]) // 64
+                np.testing.assert_array_equal(kpos, 64 * j + np.arange(nk))
+                np.testing.assert_array_equal(vis, kpos <= pos)
+                if vis.any():
+                    js.append(j)
+            assert js == list(range(pos // 64 + 1)), (t, js)
 
 
 @pytest.mark.parametrize("k", range(len(DESCS)), ids=[d[0] for d in DESCS])
@@ -225,13 +289,14 @@ def test_long_row_chunks_schedule_rows(lib):
                     continue
                 tr = qr + (t - qf)
                 row = np.zeros(idx.num_kv_tokens, np.int16)
-                for k0, nk, masked in sch["key_tiles"][kb:ke]:
-                    keys = np.arange(k0, k0 + nk)
+                for i in range(kb, ke):
+                    _, nk, masked, lo, hi, _, _ = sch["key_tiles"][i]
+                    keys = key_tile_rows(sch, i)
                     if masked:
-                        vis = (pre[keys] <= pre[tr]) & (pre[tr] < end[keys])
+                        vis = (lo <= pre[tr] < hi) & (pre[keys] <= pre[tr]) & (pre[tr] < end[keys])
                     else:
                         vis = np.ones(nk, bool)
-                    row[k0:k0 + nk] += vis
+                    np.add.at(row, keys, vis)
                 want = OT.dense_mask(idx, toks, [t])[0]
                 np.testing.assert_array_equal(row, want.astype(np.int16))
 
