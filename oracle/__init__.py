@@ -12,13 +12,18 @@ It is a plain, slow, obviously correct restatement of what the pages define:
                        tree blocks"; section 01 "Batch and prefix tree");
 * ``oracle.attention`` dense-mask softmax attention in float64;
 * ``oracle.decision``  the two-order decision and temperature calibration
-                       (architecture page, section 02 "Basal protocol").
+                       (architecture page, section 02 "Basal protocol");
+* ``oracle.rope``      rotary position embedding at the tokens' prompt
+                       positions (architecture page, section 03; AstrAI's
+                       inference guide, "Rotary Embedding Backend", "KV Cache").
 
 "The architecture page" throughout is "How basal-rs computes a decision"
 (basal.itsol.dev/en/architecture), with its Polish version
-(basal.itsol.dev/pl/architektura) used to read garbled passages.
+(basal.itsol.dev/pl/architektura) used to read garbled passages; "AstrAI's
+inference guide" is the "Inference" guide of the AstrAI repository
+(docs/guides/inference.md).
 
 Every function is pinned by ``-m "not gpu"`` tests against the pages' worked
 examples, closed forms, invariants and brute force; none is "parity unpinned".
 """
-from . import tree, attention, decision  # noqa: F401
+from . import tree, attention, decision, rope  # noqa: F401
