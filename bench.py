@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--batch-invariant", action="store_true",
                     help="key tiles by position in each query's own prompt (bitwise-identical "
                          "results alone / in a batch / in a tree) instead of the union tiling")
+    ap.add_argument("--rope", choices=["half", "interleaved"], default=None,
+                    help="rotate Q and K at the tokens' prompt positions in the cache write "
+                         "(fused rotary + cache write) before attention")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain 256 MiB device copy (known bytes) so "
                          "profiler byte counters can be scaled against it")
@@ -135,15 +138,32 @@ def main():
     torch.cuda.synchronize()
 
     n_fw = len(fw)
+    ev_w = [[torch.cuda.Event(enable_timing=True) for _ in range(n_fw)] for _ in range(args.steps)]
     ev_a = [[torch.cuda.Event(enable_timing=True) for _ in range(n_fw)] for _ in range(args.steps)]
     ev_b = [[torch.cuda.Event(enable_timing=True) for _ in range(n_fw)] for _ in range(args.steps)]
 
+    if args.rope:
+        # the usual rotary table, theta 10000, float32 (cos, sin) per position and frequency
+        max_pos = max(int(P.tree_attn_plan_export(p)["pos_id"].max()) for p in plans) + 1
+        inv = 10000.0 ** (-torch.arange(0, wl.d // 2, dtype=torch.float64) * 2.0 / wl.d)
+        ang = torch.arange(max_pos, dtype=torch.float64)[:, None] * inv[None, :]
+        rope_tab = torch.stack([ang.cos(), ang.sin()], dim=-1).float().to(dev).contiguous()
+        for x in fw:
+            x["qr"] = torch.empty_like(x["q"])
+
     def step(i=None):
         for j, (p, x) in enumerate(zip(plans, fw)):
-            P.tree_attn_cache_write(p, x["kn"], x["vn"], x["kc"], x["vc"], stream=stream)
+            if i is not None:
+                ev_w[i][j].record(stream)
+            if args.rope:
+                P.tree_attn_rope_cache_write(p, x["q"], x["qr"], x["kn"], x["vn"], rope_tab, x["kc"],
+                                             x["vc"], style=args.rope, stream=stream)
+            else:
+                P.tree_attn_cache_write(p, x["kn"], x["vn"], x["kc"], x["vc"], stream=stream)
             if i is not None:
                 ev_a[i][j].record(stream)
-            P.tree_attn_forward_cached(p, x["q"], x["kc"], x["vc"], x["o"], stream=stream)
+            P.tree_attn_forward_cached(p, x["qr"] if args.rope else x["q"], x["kc"], x["vc"], x["o"],
+                                       stream=stream)
             if i is not None:
                 ev_b[i][j].record(stream)
         P.decision_readout(logits, row1, row2, nl, temps, p_avg, p_cal, stream=stream)
@@ -170,6 +190,18 @@ def main():
     k = int(np.argmax(useful_flops))
     achieved = useful_flops[k] / (attn_ms_mean[k] * 1e-3) / 1e12
     attn_total_tflops = sum(useful_flops) / (attn_ms_mean.sum() * 1e-3) / 1e12
+    # the write kernel before each attention launch (HBM-bound): K and V read
+    # and written once, plus Q read and written and the table rows with --rope
+    write_ms = np.array([[ev_w[i][j].elapsed_time(ev_a[i][j]) for j in range(n_fw)]
+                         for i in range(args.steps)]).mean(axis=0)
+    write_bytes = []
+    for inf in infos:
+        t = inf["num_q_tokens"]
+        b = 4 * t * wl.hkv * wl.d * 2
+        if args.rope:
+            b += 2 * t * wl.hq * wl.d * 2 + t * (wl.d // 2) * 2 * 4
+        write_bytes.append(b)
+    write_gbps = sum(write_bytes) / (write_ms.sum() * 1e-3) / 1e9
 
     out = {
         "metric": "useful tree-attention TFLOP/s (packed tokens/s and % of f16 MFMA peak alongside)",
@@ -188,6 +220,10 @@ def main():
         "pct_mfma_peak": round(100 * value / PEAK_F16_TFLOPS, 2),
         "attention_only_tflops": round(attn_total_tflops, 3),
         "attention_ms_per_forward": [round(float(x), 5) for x in attn_ms_mean],
+        "cache_write": {"kernel": "rope_cache_write_kernel" if args.rope else "cache_write_kernel",
+                        "bound": "hbm", "us_per_forward": [round(float(x) * 1e3, 2) for x in write_ms],
+                        "bytes_per_forward": write_bytes, "achieved_gbps": round(write_gbps, 1),
+                        "peak_gbps": 8000.0, "frac": round(write_gbps / 8000.0, 4)},
         "plan_build_ms": round(plan_build_ms, 3),
         "config": {
             "workload": f"config[{args.config}] {wl.name}",
@@ -200,6 +236,7 @@ def main():
             "decisions": d.n_dec,
             "out_dtype": args.out_dtype,
             "key_tiling": "by prompt position" if args.batch_invariant else "union",
+            "rope": args.rope,
         },
         "roofline": {
             "bound": "mfma",
@@ -216,7 +253,8 @@ def main():
     }
 
     tr = (measured_traffic(args.config, k)
-          if args.seed == 0 and args.out_dtype == "f16" and not args.batch_invariant else None)
+          if args.seed == 0 and args.out_dtype == "f16" and not args.batch_invariant and not args.rope
+          else None)
     if tr is not None:
         out["roofline"]["traffic"] = tr["fetch_bytes"] + tr["write_bytes"]
         out["roofline"]["traffic_detail"] = dict(tr, source=os.path.relpath(TRAFFIC_FILE, ROOT))

@@ -59,6 +59,9 @@ typedef enum {
                                   K/V cache smaller than the plan's row space             */
 } ta_status;
 
+/* Element pairing of rotary embedding (see tree_attn_rope_cache_write). */
+typedef enum { TA_ROPE_HALF = 0, TA_ROPE_INTERLEAVED = 1 } ta_rope_style;
+
 typedef enum { TA_F16 = 0, TA_F32 = 1 } ta_dtype;
 
 /*
@@ -280,6 +283,35 @@ ta_status tree_attn_cache_write(ta_plan_t plan, const void* k_new, const void* v
 ta_status tree_attn_forward_cached(ta_plan_t plan, const void* q, const void* k_cache,
                                    const void* v_cache, int64_t cache_tokens, void* o, float* lse,
                                    void* hip_stream);
+
+/*
+ * Rotary embedding at tree positions fused with the cache write: the step
+ * before tree_attn_forward_cached. Each forward token t is rotated at its
+ * position id pos(t) -- its position in its own root-to-leaf prompt, the
+ * table tree_attn_plan_export reports (architecture page, section 03
+ * "Attention over tree blocks") -- and K is rotated before it is written to
+ * the cache (AstrAI's inference guide, "KV Cache"). Every element pair (a, b)
+ * of a head row, with i its pair index, becomes (a c - b s, a s + b c) for
+ * (c, s) = cos_sin[pos(t)][i] (the guide's "Rotary Embedding Backend": a
+ * [max_len, dim/2, 2] float32 table of (cos, sin), rotation as a complex
+ * multiply). Arithmetic in f32 on the f16 inputs, one rounding to f16.
+ *   q_in, q_out    [T_q, Hq, D] f16, forward order; q_out may equal q_in
+ *   k_new, v_new   [T_q, Hkv, D] f16 (unrotated K, V)
+ *   cos_sin        [max_pos, D/2, 2] f32 device, 16-byte aligned; max_pos must
+ *                  exceed the forward's largest position id
+ *   style          TA_ROPE_HALF: pair i = elements (i, i + D/2);
+ *                  TA_ROPE_INTERLEAVED: pair i = elements (2i, 2i + 1)
+ *   k_cache, v_cache [cache_tokens, Hkv, D] f16 row space: rotated K and V are
+ *                  written at each forward token's row-space index
+ *   cache_tokens   >= info.num_kv_tokens
+ * One launch on the stream. Errors: TA_ERR_INVALID_ARGUMENT (null or
+ * misaligned pointer, unknown style, max_pos too small), TA_ERR_WORKSPACE
+ * (plan not uploaded, short cache), TA_ERR_HIP.
+ */
+ta_status tree_attn_rope_cache_write(ta_plan_t plan, const void* q_in, void* q_out,
+                                     const void* k_new, const void* v_new, const float* cos_sin,
+                                     int32_t max_pos, ta_rope_style style, void* k_cache,
+                                     void* v_cache, int64_t cache_tokens, void* hip_stream);
 
 /*
  * The Basal decision (section 02 "Basal protocol"), for n_dec questions:

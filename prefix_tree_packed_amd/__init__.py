@@ -24,4 +24,5 @@ from .binding import (  # noqa: F401
     tree_attn_plan_set_max_workgroups,
     tree_attn_plan_upload,
     tree_attn_plan_workgroups,
+    tree_attn_rope_cache_write,
 )

@@ -26,7 +26,8 @@ TA_F16, TA_F32 = 0, 1
 EXPORTED = ("tree_attn_plan", "tree_attn_plan_info", "tree_attn_plan_upload",
             "tree_attn_plan_export", "tree_attn_plan_schedule", "tree_attn_plan_set_max_workgroups",
             "tree_attn_plan_workgroups", "tree_attn_plan_destroy", "tree_attn_forward",
-            "tree_attn_forward_chunked", "tree_attn_cache_write", "tree_attn_forward_cached",
+            "tree_attn_forward_chunked", "tree_attn_cache_write", "tree_attn_rope_cache_write",
+            "tree_attn_forward_cached",
             "decision_readout", "tree_attn_last_error")
 
 
@@ -92,6 +93,8 @@ def load_library(path: str = LIB_PATH):
     lib.tree_attn_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.tree_attn_forward_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, vp, vp]
     lib.tree_attn_cache_write.argtypes = [vp, vp, vp, vp, vp, i64, vp]
+    lib.tree_attn_rope_cache_write.argtypes = [vp, vp, vp, vp, vp, vp, i32, ctypes.c_int, vp, vp,
+                                               i64, vp]
     lib.tree_attn_forward_cached.argtypes = [vp, vp, vp, vp, i64, vp, vp, vp]
     lib.decision_readout.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp]
     for name in EXPORTED[:-1]:
@@ -322,6 +325,33 @@ def tree_attn_cache_write(plan: Plan, k_new, v_new, k_cache, v_cache, stream=Non
     _expect(v_cache, "v_cache", (ct, hkv, d), torch.float16)
     _check(load_library().tree_attn_cache_write(plan.handle, _vp(k_new), _vp(v_new), _vp(k_cache),
                                                 _vp(v_cache), int(ct), _stream_handle(stream)))
+
+
+ROPE_STYLES = {"half": 0, "interleaved": 1}
+
+
+def tree_attn_rope_cache_write(plan: Plan, q_in, q_out, k_new, v_new, cos_sin, k_cache, v_cache,
+                               style: str = "half", stream=None) -> None:
+    """Rotary embedding at the plan's position ids on Q (into q_out, which may
+    be q_in) and K, with rotated K and V written into the row-space cache.
+    cos_sin: float32 [max_pos, head_dim / 2, 2] table of (cos, sin)."""
+    import torch
+    info, cfg = plan.info, plan.cfg
+    nq, hq, hkv, d = info["num_q_tokens"], cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"]
+    if style not in ROPE_STYLES:
+        raise ValueError(f"style must be one of {sorted(ROPE_STYLES)}")
+    _expect(q_in, "q_in", (nq, hq, d), torch.float16)
+    _expect(q_out, "q_out", (nq, hq, d), torch.float16)
+    _expect(k_new, "k_new", (nq, hkv, d), torch.float16)
+    _expect(v_new, "v_new", (nq, hkv, d), torch.float16)
+    _expect(cos_sin, "cos_sin", (cos_sin.shape[0], d // 2, 2), torch.float32)
+    ct = k_cache.shape[0]
+    _expect(k_cache, "k_cache", (ct, hkv, d), torch.float16)
+    _expect(v_cache, "v_cache", (ct, hkv, d), torch.float16)
+    _check(load_library().tree_attn_rope_cache_write(
+        plan.handle, _vp(q_in), _vp(q_out), _vp(k_new), _vp(v_new), _vp(cos_sin),
+        int(cos_sin.shape[0]), ROPE_STYLES[style], _vp(k_cache), _vp(v_cache), int(ct),
+        _stream_handle(stream)))
 
 
 def tree_attn_forward_cached(plan: Plan, q, k_cache, v_cache, o, lse=None, stream=None) -> None:

@@ -123,6 +123,45 @@ ta_status tree_attn_cache_write(ta_plan_t p, const void* k_new, const void* v_ne
   return TA_OK;
 }
 
+ta_status tree_attn_rope_cache_write(ta_plan_t p, const void* q_in, void* q_out, const void* k_new,
+                                     const void* v_new, const float* cos_sin, int32_t max_pos,
+                                     ta_rope_style style, void* k_cache, void* v_cache,
+                                     int64_t cache_tokens, void* hip_stream) {
+  ta::clear_error();
+  if (p && p->n_q == 0) return TA_OK;
+  const void* ptrs[] = {q_in, q_out, k_new, v_new, cos_sin, k_cache, v_cache};
+  const char* names[] = {"q_in", "q_out", "k_new", "v_new", "cos_sin", "k_cache", "v_cache"};
+  ta_status st = ta::check_tensors(p, ptrs, names, 7, nullptr);
+  if (st != TA_OK) return st;
+  if (style != TA_ROPE_HALF && style != TA_ROPE_INTERLEAVED)
+    return ta::fail(TA_ERR_INVALID_ARGUMENT, "unknown rope style %d", (int)style);
+  if (max_pos <= p->max_pos_id)
+    return ta::fail(TA_ERR_INVALID_ARGUMENT, "cos_sin has %d positions; this forward needs position %d",
+                    max_pos, p->max_pos_id);
+  if (cache_tokens < p->n_kv)
+    return ta::fail(TA_ERR_WORKSPACE, "cache holds %lld tokens < %lld of the plan's row space",
+                    (long long)cache_tokens, (long long)p->n_kv);
+  const unsigned char* ws = (const unsigned char*)p->d_ws;
+  ta::RopeArgs a;
+  a.q_in = q_in;
+  a.q_out = q_out;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.cos_sin = cos_sin;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.tok_rowpos = ws + p->off_rowpos;
+  a.pos_id = ws + p->off_posid;
+  a.n_q = (int)p->n_q;
+  a.hq = p->cfg.num_q_heads;
+  a.hkv = p->cfg.num_kv_heads;
+  a.head_dim = p->cfg.head_dim;
+  a.interleaved = style == TA_ROPE_INTERLEAVED;
+  hipError_t e = ta::launch_rope_cache_write(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return ta::hip_fail(e, "rope cache write launch");
+  return TA_OK;
+}
+
 ta_status tree_attn_forward_cached(ta_plan_t p, const void* q, const void* k_cache, const void* v_cache,
                                    int64_t cache_tokens, void* o, float* lse, void* hip_stream) {
   ta::clear_error();

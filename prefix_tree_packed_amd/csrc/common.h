@@ -51,7 +51,8 @@ struct ta_plan_s {
 
   size_t off_qtiles = 0, off_ktiles = 0, off_kvis = 0, off_segs = 0, off_work = 0, off_anc = 0,
          off_rowpos = 0;
-  size_t off_wg_ptr = 0, off_wg_items = 0;
+  size_t off_wg_ptr = 0, off_wg_items = 0, off_posid = 0;
+  int32_t max_pos_id = -1;          // largest position id of this forward's tokens
   size_t ws_bytes = 0;
   std::vector<unsigned char> image;
 

@@ -30,6 +30,20 @@ int attention_blocks_per_cu(int head_dim, int group, bool out_f32);
 hipError_t launch_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                               const void* tok_rowpos, int n_q, int hkv, int head_dim,
                               hipStream_t st);
+struct RopeArgs {
+  const void* q_in;
+  void* q_out;
+  const void* k_new;
+  const void* v_new;
+  const float* cos_sin;
+  void* k_cache;
+  void* v_cache;
+  const void* tok_rowpos;
+  const void* pos_id;
+  int n_q, hq, hkv, head_dim;
+  bool interleaved;
+};
+hipError_t launch_rope_cache_write(const RopeArgs& a, hipStream_t st);
 hipError_t launch_decision(const float* logits, int n_rows, int ld, const int* row1, const int* row2,
                            const int* n_letters, const float* T, int n_dec, float* p_avg,
                            float* p_cal, hipStream_t st);

@@ -233,6 +233,7 @@ void Builder::token_tables() {
   p->tok_anc.assign(p->n_kv + kKeyTile, Int2{0, 0});
   p->useful_pairs = 0;
   p->cost_separate = 0;
+  p->max_pos_id = -1;
   p->leaf_block.clear();
   p->leaf_tok.clear();
   for (int r = 0; r < (int)rows.size(); ++r) {
@@ -245,6 +246,7 @@ void Builder::token_tables() {
         const int64_t t = v.q_off + (i - v.qb);
         const int32_t pos = anc_len[g] + (i - s);
         p->pos_id[t] = pos;
+        p->max_pos_id = std::max(p->max_pos_id, pos);
         p->tok_row[t] = r;
         p->tok_block[t] = g;
         p->tok_offset[t] = i - s;
@@ -551,6 +553,8 @@ static void build_image(ta_plan_s* p) {
   off = align256(off + p->tok_anc.size() * sizeof(Int2));
   p->off_rowpos = off;
   off = align256(off + p->tok_rowpos.size() * sizeof(int32_t));
+  p->off_posid = off;
+  off = align256(off + p->pos_id.size() * sizeof(int32_t));
   // filled by the upload, once the device's workgroup count is known
   p->off_wg_ptr = off;
   off = align256(off + (kMaxWorkgroups + 1) * sizeof(int32_t));
@@ -568,6 +572,7 @@ static void build_image(ta_plan_s* p) {
   put(p->off_work, p->work.data(), p->work.size() * sizeof(int32_t));
   put(p->off_anc, p->tok_anc.data(), p->tok_anc.size() * sizeof(Int2));
   put(p->off_rowpos, p->tok_rowpos.data(), p->tok_rowpos.size() * sizeof(int32_t));
+  put(p->off_posid, p->pos_id.data(), p->pos_id.size() * sizeof(int32_t));
 }
 
 ta_status build_plan(const ta_tree_desc* desc, const ta_attn_cfg* cfg, ta_plan_s* p) {
