@@ -15,7 +15,9 @@ It is a plain, slow, obviously correct restatement of what the pages define:
                        (architecture page, section 02 "Basal protocol");
 * ``oracle.rope``      rotary position embedding at the tokens' prompt
                        positions (architecture page, section 03; AstrAI's
-                       inference guide, "Rotary Embedding Backend", "KV Cache").
+                       inference guide, "Rotary Embedding Backend", "KV Cache");
+* ``oracle.packing``   tokenized prompts into prefix-tree rows, request cost,
+                       batch formation (architecture page, sections 01, 03, 04).
 
 "The architecture page" throughout is "How basal-rs computes a decision"
 (basal.itsol.dev/en/architecture), with its Polish version
@@ -26,4 +28,4 @@ inference guide" is the "Inference" guide of the AstrAI repository
 Every function is pinned by ``-m "not gpu"`` tests against the pages' worked
 examples, closed forms, invariants and brute force; none is "parity unpinned".
 """
-from . import tree, attention, decision, rope  # noqa: F401
+from . import tree, attention, decision, rope, packing  # noqa: F401
