@@ -335,6 +335,78 @@ ta_status decision_readout(const float* logits, int32_t n_rows, int32_t ld, cons
                            const int32_t* row2, const int32_t* n_letters, const float* T,
                            int32_t n_dec, float* p_avg, float* p_cal, void* hip_stream);
 
+/*
+ * Packing a batch's tokenized prompts into rows of prefix trees: the producer
+ * of the ta_tree_desc a forward is planned from (architecture page, section 01
+ * "Batch and prefix tree": prompts arranged into rows, each a tree whose shared
+ * prefixes are computed once, rows up to 32,768 tokens, trees up to 8 blocks
+ * deep, identical prompts sharing one readout; section 03 "Packing": template
+ * -> state -> question -> option order blocks). Host only.
+ * A row's tree is a trie over token ids cut into blocks at every branch point,
+ * every prompt's last token and every part boundary the caller marks (so
+ * template, state, question and option order stay separate blocks); blocks are
+ * laid out depth-first, children in the order their first prompt arrived.
+ * Prompts join rows in order; one that would take the current row past
+ * max_row_tokens tokens or max_depth blocks starts the next row.
+ *   tokens        [prompt_indptr[n_prompts]] int32 token ids, prompts concatenated
+ *   prompt_indptr [n_prompts + 1] int64, prompt_indptr[0] = 0, every prompt >= 1 token
+ *   part_lens, part_indptr  optional (both NULL, or both given): prompt i's parts
+ *                 are part_lens[part_indptr[i] .. part_indptr[i+1]), each >= 1,
+ *                 summing to its length (no parts: the prompt is one part)
+ * All arrays are host memory, read during the call only. *out receives a
+ * handle owned by the caller (free it with tree_pack_destroy); on error *out is
+ * set to NULL and nothing stays allocated.
+ * Errors: TA_ERR_INVALID_ARGUMENT (NULL, empty prompt, parts that do not split
+ * a prompt, limits < 1), TA_ERR_LIMIT (a prompt alone exceeds the limits).
+ */
+typedef struct ta_pack_s* ta_pack_t;
+
+typedef struct {
+  int64_t num_prompts;
+  int32_t num_rows;
+  int32_t num_blocks;       /* over all rows                                  */
+  int64_t num_tokens;       /* packed tokens over all rows                    */
+  int64_t separate_tokens;  /* tokens of all prompts run one by one           */
+} ta_pack_info;
+
+ta_status tree_pack(const int32_t* tokens, const int64_t* prompt_indptr, const int32_t* part_lens,
+                    const int64_t* part_indptr, int32_t n_prompts, int32_t max_row_tokens,
+                    int32_t max_depth, ta_pack_t* out);
+ta_status tree_pack_info(ta_pack_t pack, ta_pack_info* out);
+/*
+ * The packed rows, in the layout ta_tree_desc takes (block_parent is the
+ * parent's index within its row, -1 for a root), plus where each prompt reads
+ * out. Each pointer may be NULL.
+ *   row_block_indptr [num_rows + 1]; block_parent, block_len [num_blocks];
+ *   row_tokens [num_tokens]: the rows' token ids in layout order, rows concatenated;
+ *   prompt_row, prompt_block, prompt_readout [num_prompts]: prompt i's row, its
+ *   last block (row-local index), and the row-local index of its last token
+ *   (the last token of that block; identical prompts get the same three).
+ */
+ta_status tree_pack_export(ta_pack_t pack, int32_t* row_block_indptr, int32_t* block_parent,
+                           int32_t* block_len, int32_t* row_tokens, int32_t* prompt_row,
+                           int32_t* prompt_block, int32_t* prompt_readout);
+/* Free a pack. NULL is a no-op. */
+ta_status tree_pack_destroy(ta_pack_t pack);
+
+/*
+ * A request's cost (section 01 "Validation and planning"): the tokens its
+ * prompts need with shared prefixes counted once, not counting the first
+ * cached_prefix tokens of each prompt (a template computed once at start-up).
+ * Errors: TA_ERR_INVALID_ARGUMENT.
+ */
+ta_status tree_request_cost(const int32_t* tokens, const int64_t* prompt_indptr, int32_t n_prompts,
+                            int32_t cached_prefix, int64_t* cost);
+
+/*
+ * Batch formation (sections 01 and 04: a batch is the first queued request
+ * and each subsequent request that fits within max_batch_tokens, 8,192):
+ * batch[i] = index of request i's batch, requests in queue order, a request
+ * fitting if the batch's summed costs stay <= limit (the first request of a
+ * batch always forms it). Errors: TA_ERR_INVALID_ARGUMENT (NULL, cost < 0).
+ */
+ta_status tree_form_batches(const int64_t* costs, int32_t n, int64_t limit, int32_t* batch);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* tree_attn_last_error(void);
 

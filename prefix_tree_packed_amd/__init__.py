@@ -25,4 +25,7 @@ from .binding import (  # noqa: F401
     tree_attn_plan_upload,
     tree_attn_plan_workgroups,
     tree_attn_rope_cache_write,
+    tree_form_batches,
+    tree_pack,
+    tree_request_cost,
 )

@@ -28,7 +28,8 @@ EXPORTED = ("tree_attn_plan", "tree_attn_plan_info", "tree_attn_plan_upload",
             "tree_attn_plan_workgroups", "tree_attn_plan_destroy", "tree_attn_forward",
             "tree_attn_forward_chunked", "tree_attn_cache_write", "tree_attn_rope_cache_write",
             "tree_attn_forward_cached",
-            "decision_readout", "tree_attn_last_error")
+            "tree_pack", "tree_pack_info", "tree_pack_export", "tree_pack_destroy",
+            "tree_request_cost", "tree_form_batches", "decision_readout", "tree_attn_last_error")
 
 
 class TreeAttnError(RuntimeError):
@@ -67,6 +68,12 @@ class _PlanInfo(ctypes.Structure):
                 ("pad0", ctypes.c_int32)]
 
 
+class _PackInfo(ctypes.Structure):
+    _fields_ = [("num_prompts", ctypes.c_int64), ("num_rows", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("num_tokens", ctypes.c_int64),
+                ("separate_tokens", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -97,6 +104,13 @@ def load_library(path: str = LIB_PATH):
                                                i64, vp]
     lib.tree_attn_forward_cached.argtypes = [vp, vp, vp, vp, i64, vp, vp, vp]
     lib.decision_readout.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp]
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    lib.tree_pack.argtypes = [p32, p64, p32, p64, i32, i32, i32, ctypes.POINTER(vp)]
+    lib.tree_pack_info.argtypes = [vp, ctypes.POINTER(_PackInfo)]
+    lib.tree_pack_export.argtypes = [vp, p32, p32, p32, p32, p32, p32, p32]
+    lib.tree_pack_destroy.argtypes = [vp]
+    lib.tree_request_cost.argtypes = [p32, p64, i32, i32, p64]
+    lib.tree_form_batches.argtypes = [p64, i32, i64, p32]
     for name in EXPORTED[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.tree_attn_last_error.restype = ctypes.c_char_p
@@ -379,3 +393,68 @@ def decision_readout(logits, row1, row2, n_letters, T, p_avg, p_cal, stream=None
     _check(load_library().decision_readout(_vp(logits), int(n_rows), int(ld), _vp(row1), _vp(row2),
                                            _vp(n_letters), _vp(T), int(n_dec), _vp(p_avg), _vp(p_cal),
                                            _stream_handle(stream)))
+
+
+# ---------------------------------------------------------------------------
+# packing tokenized prompts into prefix-tree rows, request cost, batches
+# ---------------------------------------------------------------------------
+
+def _ptr64(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def _concat(prompts):
+    lens = np.asarray([len(p) for p in prompts], np.int64)
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    toks = (np.concatenate([np.asarray(p, np.int32) for p in prompts]).astype(np.int32)
+            if len(prompts) else np.zeros(0, np.int32))
+    return np.ascontiguousarray(toks), np.ascontiguousarray(indptr)
+
+
+def tree_pack(prompts, parts=None, max_row_tokens: int = 32768, max_depth: int = 8) -> dict:
+    """Pack tokenized prompts (sequences of token ids) into prefix-tree rows.
+    parts[i] optionally lists prompt i's part lengths. Returns the rows in
+    ta_tree_desc layout (row_block_indptr, block_parent, block_len), the row
+    tokens and each prompt's (row, block, row-local readout index)."""
+    lib = load_library()
+    toks, indptr = _concat(prompts)
+    pl = pi = None
+    if parts is not None:
+        pl, pi = _concat(parts)
+    h = ctypes.c_void_p()
+    _check(lib.tree_pack(_ptr32(toks), _ptr64(indptr), _ptr32(pl), _ptr64(pi), len(prompts),
+                         int(max_row_tokens), int(max_depth), ctypes.byref(h)))
+    try:
+        info = _PackInfo()
+        _check(lib.tree_pack_info(h, ctypes.byref(info)))
+        out = {"row_block_indptr": np.zeros(info.num_rows + 1, np.int32),
+               "block_parent": np.zeros(info.num_blocks, np.int32),
+               "block_len": np.zeros(info.num_blocks, np.int32),
+               "row_tokens": np.zeros(info.num_tokens, np.int32),
+               "prompt_row": np.zeros(info.num_prompts, np.int32),
+               "prompt_block": np.zeros(info.num_prompts, np.int32),
+               "prompt_readout": np.zeros(info.num_prompts, np.int32)}
+        _check(lib.tree_pack_export(h, *(_ptr32(out[k]) for k in (
+            "row_block_indptr", "block_parent", "block_len", "row_tokens", "prompt_row",
+            "prompt_block", "prompt_readout"))))
+        out["separate_tokens"] = int(info.separate_tokens)
+        return out
+    finally:
+        lib.tree_pack_destroy(h)
+
+
+def tree_request_cost(prompts, cached_prefix: int = 0) -> int:
+    lib = load_library()
+    toks, indptr = _concat(prompts)
+    cost = ctypes.c_int64()
+    _check(lib.tree_request_cost(_ptr32(toks), _ptr64(indptr), len(prompts), int(cached_prefix),
+                                 ctypes.byref(cost)))
+    return int(cost.value)
+
+
+def tree_form_batches(costs, limit: int = 8192) -> np.ndarray:
+    lib = load_library()
+    c = np.ascontiguousarray(np.asarray(costs, np.int64))
+    out = np.zeros(len(c), np.int32)
+    _check(lib.tree_form_batches(_ptr64(c), len(c), int(limit), _ptr32(out)))
+    return out
