@@ -17,7 +17,10 @@ It is a plain, slow, obviously correct restatement of what the pages define:
                        positions (architecture page, section 03; AstrAI's
                        inference guide, "Rotary Embedding Backend", "KV Cache");
 * ``oracle.packing``   tokenized prompts into prefix-tree rows, request cost,
-                       batch formation (architecture page, sections 01, 03, 04).
+                       batch formation (architecture page, sections 01, 03, 04);
+* ``oracle.readout``   the last layer's MLP block and answer-letter logits
+                       at readout rows only, float16 storage points (architecture
+                       page, sections 01 and 05).
 
 "The architecture page" throughout is "How basal-rs computes a decision"
 (basal.itsol.dev/en/architecture), with its Polish version
@@ -28,4 +31,4 @@ inference guide" is the "Inference" guide of the AstrAI repository
 Every function is pinned by ``-m "not gpu"`` tests against the pages' worked
 examples, closed forms, invariants and brute force; none is "parity unpinned".
 """
-from . import tree, attention, decision, rope, packing  # noqa: F401
+from . import tree, attention, decision, rope, packing, readout  # noqa: F401
