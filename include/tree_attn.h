@@ -53,7 +53,8 @@ typedef enum {
                                   misaligned buffer, call not valid for this plan      */
   TA_ERR_INVALID_TREE = 2,     /* empty row, block length < 1, parent not in [-1, self) */
   TA_ERR_LIMIT = 3,            /* row > 32768 tokens, forward > 8192 tokens, depth > 8,
-                                  head_dim not 64/128, heads per KV head not 1/2/4/8      */
+                                  head_dim not 64/128, heads per KV head not 1/2/4/8,
+                                  readout model sizes outside their stated ranges       */
   TA_ERR_HIP = 4,              /* a HIP runtime call failed (message has its text)       */
   TA_ERR_WORKSPACE = 5         /* plan not uploaded, workspace too small or misaligned,
                                   K/V cache smaller than the plan's row space             */
@@ -312,6 +313,95 @@ ta_status tree_attn_rope_cache_write(ta_plan_t plan, const void* q_in, void* q_o
                                      const void* k_new, const void* v_new, const float* cos_sin,
                                      int32_t max_pos, ta_rope_style style, void* k_cache,
                                      void* v_cache, int64_t cache_tokens, void* hip_stream);
+
+/*
+ * Readout-only last layer (architecture page, section 01 stage "GPU forward
+ * pass": in the final layer the MLP block and the logits are computed only for
+ * readout positions and answer letters; section 05, f16 default row: residual
+ * stream, normalizations and MLP blocks in f16 with f32 accumulation in matrix
+ * products; "Batch-independent GEMM table": a custom kernel reads the letters
+ * out and letter logits are bitwise identical whatever shares the batch).
+ *
+ * readout_mlp: the Llama MLP block with its residual, at readout rows only.
+ * For readout row m with token t = readout_tok[m] and h = hidden[t]:
+ *   xn  = f16(h * (mean(h^2) + eps)^(-1/2) * norm_w)
+ *   act = f16(silu(f16(xn . w_gate^T)) * f16(xn . w_up^T)),  silu(z) = z / (1 + e^-z)
+ *   h_out[m] = f16(h + f16(act . w_down^T))
+ * (each product accumulated in f32; each f16() one rounding to nearest even).
+ *   hidden      [n_tokens, d_model] f16 device: the residual stream entering the
+ *               last layer's MLP block (after its attention and residual add)
+ *   readout_tok [n_readout] int32 device: token row of each readout; a row may
+ *               repeat (identical prompts share a readout); an entry outside
+ *               [0, n_tokens) gives a NaN row (checked by the kernels, no access)
+ *   w           weights, all f16 device, row-major in the linear-layer layout
+ *               (output = input . W^T): norm_w [d_model]; w_gate_up [2 d_ff,
+ *               d_model], the gate and up matrices interleaved in blocks of 8
+ *               rows (rows 16i .. 16i+7 = gate rows 8i .. 8i+7, rows 16i+8 ..
+ *               16i+15 = up rows 8i .. 8i+7; readout_pack_gate_up writes it);
+ *               w_down [d_model, d_ff]; d_model a multiple of 256 up to 16384,
+ *               d_ff a multiple of 256
+ *   workspace   device, at least readout_mlp_workspace_size() bytes, 16-byte
+ *               aligned; on return it holds xn [n_readout, d_model] f16 at byte 0
+ *               and act [n_readout, d_ff] f16 at byte round_up(n_readout * d_model
+ *               * 2, 256), then f32 partial sums of the down product
+ *   h_out       [n_readout, d_model] f16 device output
+ * The down product's K range is split into a fixed number of parts chosen from
+ * (d_model, d_ff) alone and summed in part order, so every row's result is the
+ * same whatever n_readout and the other rows are. Calls on one stream are
+ * ordered; the workspace must not be shared by calls that may overlap.
+ * Errors: TA_ERR_INVALID_ARGUMENT (NULL or misaligned pointer, n_readout < 0,
+ * n_tokens < 1, eps < 0), TA_ERR_LIMIT (sizes), TA_ERR_WORKSPACE (too small),
+ * TA_ERR_HIP. n_readout = 0 launches nothing.
+ */
+typedef struct {
+  int32_t d_model;
+  int32_t d_ff;
+  float eps;
+  int32_t pad0;
+  const void* norm_w;
+  const void* w_gate_up;
+  const void* w_down;
+} ta_mlp_weights;
+
+/*
+ * The gate/up layout readout_mlp reads (a one-time conversion when weights are
+ * loaded): w_gate_up[16i + r] = w_gate[8i + r] for r < 8, w_up[8i + r - 8] for
+ * r >= 8. Interleaving makes the projection one stream of consecutive rows;
+ * two matrices read in lockstep contend for the same HBM channels when their
+ * addresses are an unlucky distance apart (measured: up to half the
+ * bandwidth). w_gate, w_up [d_ff, d_model] f16 device; w_gate_up [2 d_ff,
+ * d_model] f16 device output (must not overlap the inputs). Sizes as in
+ * readout_mlp. Errors: TA_ERR_INVALID_ARGUMENT, TA_ERR_LIMIT, TA_ERR_HIP.
+ */
+ta_status readout_pack_gate_up(const void* w_gate, const void* w_up, int32_t d_ff, int32_t d_model,
+                               void* w_gate_up, void* hip_stream);
+
+ta_status readout_mlp_workspace_size(int32_t n_readout, int32_t d_model, int32_t d_ff, size_t* bytes);
+ta_status readout_mlp(const void* hidden, int64_t n_tokens, const int32_t* readout_tok,
+                      int32_t n_readout, const ta_mlp_weights* w, void* workspace,
+                      size_t workspace_bytes, void* h_out, void* hip_stream);
+
+/*
+ * letter_logits: the final RMS norm of each readout row and the logits of its
+ * answer letters only (rows of the language-model head):
+ *   y = f16(h[m] * (mean(h[m]^2) + eps)^(-1/2) * final_norm_w)
+ *   logits[m][j] = sum_k lm_head[letter_ids[m][j]][k] * y[k]   (f32, unrounded)
+ * for j < n_letters[m]; logits[m][j] = 0 for n_letters[m] <= j < ld. The sum
+ * runs in a fixed order per row (batch-independent).
+ *   h            [n_readout, d_model] f16 device (readout_mlp's h_out), d_model a
+ *                multiple of 8 up to 16384
+ *   final_norm_w [d_model] f16 device; lm_head [vocab, d_model] f16 device (only
+ *                the letters' rows are read)
+ *   letter_ids   [n_readout, ld] int32 device; n_letters [n_readout] int32 device
+ *   logits       [n_readout, ld] f32 device output, the layout decision_readout
+ *                takes; ld in [1, 255]
+ * Device values are checked by the kernel: a row with n_letters outside [1, ld]
+ * gets NaN in every column, a letter id outside [0, vocab) a NaN logit.
+ * Errors: TA_ERR_INVALID_ARGUMENT, TA_ERR_LIMIT (d_model), TA_ERR_HIP.
+ */
+ta_status letter_logits(const void* h, int32_t n_readout, int32_t d_model, const void* final_norm_w,
+                        float eps, const void* lm_head, int32_t vocab, const int32_t* letter_ids,
+                        const int32_t* n_letters, int32_t ld, float* logits, void* hip_stream);
 
 /*
  * The Basal decision (section 02 "Basal protocol"), for n_dec questions:

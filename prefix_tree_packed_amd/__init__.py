@@ -10,7 +10,12 @@ from .binding import (  # noqa: F401
     Plan,
     TreeAttnError,
     decision_readout,
+    letter_logits,
     load_library,
+    readout_mlp,
+    readout_mlp_workspace_size,
+    readout_pack_gate_up,
+    readout_workspace_views,
     tree_attn_cache_write,
     tree_attn_forward,
     tree_attn_forward_cached,

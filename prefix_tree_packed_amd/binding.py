@@ -29,7 +29,8 @@ EXPORTED = ("tree_attn_plan", "tree_attn_plan_info", "tree_attn_plan_upload",
             "tree_attn_forward_chunked", "tree_attn_cache_write", "tree_attn_rope_cache_write",
             "tree_attn_forward_cached",
             "tree_pack", "tree_pack_info", "tree_pack_export", "tree_pack_destroy",
-            "tree_request_cost", "tree_form_batches", "decision_readout", "tree_attn_last_error")
+            "tree_request_cost", "tree_form_batches", "readout_mlp_workspace_size", "readout_mlp", "readout_pack_gate_up",
+            "letter_logits", "decision_readout", "tree_attn_last_error")
 
 
 class TreeAttnError(RuntimeError):
@@ -77,6 +78,12 @@ class _PackInfo(ctypes.Structure):
 _lib = None
 
 
+class _MlpWeights(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("pad0", ctypes.c_int32), ("norm_w", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p)]
+
+
 def load_library(path: str = LIB_PATH):
     """Load libtreeattn.so once. torch is imported first so that the library
     binds to the HIP runtime torch already loaded (one runtime per process)."""
@@ -111,6 +118,10 @@ def load_library(path: str = LIB_PATH):
     lib.tree_pack_destroy.argtypes = [vp]
     lib.tree_request_cost.argtypes = [p32, p64, i32, i32, p64]
     lib.tree_form_batches.argtypes = [p64, i32, i64, p32]
+    lib.readout_mlp_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.readout_mlp.argtypes = [vp, i64, vp, i32, ctypes.POINTER(_MlpWeights), vp, ctypes.c_size_t, vp, vp]
+    lib.readout_pack_gate_up.argtypes = [vp, vp, i32, i32, vp, vp]
+    lib.letter_logits.argtypes = [vp, i32, i32, vp, ctypes.c_float, vp, i32, vp, vp, i32, vp, vp]
     for name in EXPORTED[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.tree_attn_last_error.restype = ctypes.c_char_p
@@ -393,6 +404,93 @@ def decision_readout(logits, row1, row2, n_letters, T, p_avg, p_cal, stream=None
     _check(load_library().decision_readout(_vp(logits), int(n_rows), int(ld), _vp(row1), _vp(row2),
                                            _vp(n_letters), _vp(T), int(n_dec), _vp(p_avg), _vp(p_cal),
                                            _stream_handle(stream)))
+
+
+# ---------------------------------------------------------------------------
+# readout-only last layer: MLP block at readout rows, answer-letter logits
+# ---------------------------------------------------------------------------
+
+def readout_mlp_workspace_size(n_readout: int, d_model: int, d_ff: int) -> int:
+    out = ctypes.c_size_t()
+    _check(load_library().readout_mlp_workspace_size(int(n_readout), int(d_model), int(d_ff),
+                                                     ctypes.byref(out)))
+    return int(out.value)
+
+
+def readout_workspace_views(workspace, n_readout: int, d_model: int, d_ff: int):
+    """(xn [n, d_model], act [n, d_ff]) f16 views of a readout_mlp workspace."""
+    import torch
+    b = workspace.view(torch.uint8)
+    nx = n_readout * d_model * 2
+    off = (nx + 255) // 256 * 256
+    xn = b[:nx].view(torch.float16).view(n_readout, d_model)
+    act = b[off:off + n_readout * d_ff * 2].view(torch.float16).view(n_readout, d_ff)
+    return xn, act
+
+
+def readout_pack_gate_up(w_gate, w_up, out=None, stream=None):
+    """The interleaved [2 d_ff, d_model] gate/up matrix readout_mlp reads."""
+    import torch
+    ff, dm = w_gate.shape
+    _expect(w_gate, "w_gate", (ff, dm), torch.float16)
+    _expect(w_up, "w_up", (ff, dm), torch.float16)
+    if out is None:
+        out = torch.empty((2 * ff, dm), dtype=torch.float16, device=w_gate.device)
+    _expect(out, "w_gate_up", (2 * ff, dm), torch.float16)
+    _check(load_library().readout_pack_gate_up(_vp(w_gate), _vp(w_up), int(ff), int(dm), _vp(out),
+                                               _stream_handle(stream)))
+    return out
+
+
+def readout_mlp(hidden, readout_tok, norm_w, w_gate_up, w_down, h_out, eps: float = 1e-5,
+                workspace=None, stream=None):
+    """MLP block with its residual at the readout rows of hidden [n_tokens, d_model]
+    (f16): h_out [n_readout, d_model] f16. w_gate_up is readout_pack_gate_up's
+    layout. Returns the workspace (uint8 tensor)."""
+    import torch
+    if hidden.dim() != 2:
+        raise ValueError("hidden must be [n_tokens, d_model]")
+    n_tok, dm = hidden.shape
+    ff = w_gate_up.shape[0] // 2
+    n = readout_tok.shape[0]
+    _expect(hidden, "hidden", (n_tok, dm), torch.float16)
+    _expect(readout_tok, "readout_tok", (n,), torch.int32)
+    _expect(norm_w, "norm_w", (dm,), torch.float16)
+    _expect(w_gate_up, "w_gate_up", (2 * ff, dm), torch.float16)
+    _expect(w_down, "w_down", (dm, ff), torch.float16)
+    _expect(h_out, "h_out", (n, dm), torch.float16)
+    need = readout_mlp_workspace_size(n, dm, ff)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=hidden.device)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_cuda:
+        raise ValueError("workspace must be a 1-D uint8 GPU tensor")
+    w = _MlpWeights(int(dm), int(ff), float(eps), 0, norm_w.data_ptr(), w_gate_up.data_ptr(),
+                    w_down.data_ptr())
+    _check(load_library().readout_mlp(_vp(hidden), int(n_tok), _vp(readout_tok), int(n), ctypes.byref(w),
+                                      _vp(workspace), int(workspace.numel()), _vp(h_out),
+                                      _stream_handle(stream)))
+    return workspace
+
+
+def letter_logits(h, final_norm_w, lm_head, letter_ids, n_letters, logits, eps: float = 1e-5,
+                  stream=None) -> None:
+    """Final RMS norm of readout rows h [n, d_model] (f16) and the logits of each
+    row's letters: logits [n, ld] f32 (the layout decision_readout takes)."""
+    import torch
+    if h.dim() != 2 or logits.dim() != 2:
+        raise ValueError("h must be [n, d_model] and logits [n, ld]")
+    n, dm = h.shape
+    ld = logits.shape[1]
+    vocab = lm_head.shape[0]
+    _expect(h, "h", (n, dm), torch.float16)
+    _expect(final_norm_w, "final_norm_w", (dm,), torch.float16)
+    _expect(lm_head, "lm_head", (vocab, dm), torch.float16)
+    _expect(letter_ids, "letter_ids", (n, ld), torch.int32)
+    _expect(n_letters, "n_letters", (n,), torch.int32)
+    _expect(logits, "logits", (n, ld), torch.float32)
+    _check(load_library().letter_logits(_vp(h), int(n), int(dm), _vp(final_norm_w), float(eps),
+                                        _vp(lm_head), int(vocab), _vp(letter_ids), _vp(n_letters),
+                                        int(ld), _vp(logits), _stream_handle(stream)))
 
 
 # ---------------------------------------------------------------------------

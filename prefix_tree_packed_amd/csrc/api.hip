@@ -214,3 +214,153 @@ ta_status decision_readout(const float* logits, int32_t n_rows, int32_t ld, cons
 }
 
 }  // extern "C"
+
+namespace ta {
+
+constexpr int kReadoutMaxModel = 16384;
+
+// K splits of the down projection: a function of the weight shape only (so a
+// row's sums never depend on the batch), enough to give about 512 workgroups.
+static int readout_splits(int d_model, int d_ff) {
+  const int col_blocks = d_model / 64;
+  int ks = 8;
+  while (ks > 1 && (ks * col_blocks > 512 || d_ff % (ks * 256) != 0)) ks /= 2;
+  return ks;
+}
+
+static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct ReadoutLayout {
+  size_t xn, act, partial, total;
+  int splits;
+};
+
+static ReadoutLayout readout_layout(int n, int d_model, int d_ff) {
+  ReadoutLayout l;
+  l.splits = readout_splits(d_model, d_ff);
+  l.xn = 0;
+  l.act = round256((size_t)n * d_model * 2);
+  l.partial = l.act + round256((size_t)n * d_ff * 2);
+  l.total = l.partial + (size_t)l.splits * n * d_model * 4;
+  return l;
+}
+
+static ta_status check_mlp_shape(int32_t n, int32_t d_model, int32_t d_ff) {
+  if (n < 0) return fail(TA_ERR_INVALID_ARGUMENT, "n_readout %d < 0", n);
+  if (d_model < 256 || d_model > kReadoutMaxModel || d_model % 256)
+    return fail(TA_ERR_LIMIT, "d_model %d is not a multiple of 256 in [256, %d]", d_model,
+                kReadoutMaxModel);
+  if (d_ff < 256 || d_ff % 256) return fail(TA_ERR_LIMIT, "d_ff %d is not a multiple of 256", d_ff);
+  return TA_OK;
+}
+
+}  // namespace ta
+
+extern "C" {
+
+ta_status readout_mlp_workspace_size(int32_t n_readout, int32_t d_model, int32_t d_ff, size_t* bytes) {
+  ta::clear_error();
+  if (!bytes) return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL argument");
+  ta_status st = ta::check_mlp_shape(n_readout, d_model, d_ff);
+  if (st != TA_OK) return st;
+  *bytes = ta::readout_layout(n_readout, d_model, d_ff).total;
+  return TA_OK;
+}
+
+ta_status readout_mlp(const void* hidden, int64_t n_tokens, const int32_t* readout_tok,
+                      int32_t n_readout, const ta_mlp_weights* w, void* workspace,
+                      size_t workspace_bytes, void* h_out, void* hip_stream) {
+  ta::clear_error();
+  if (!w) return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL weights");
+  ta_status st = ta::check_mlp_shape(n_readout, w->d_model, w->d_ff);
+  if (st != TA_OK) return st;
+  if (n_readout == 0) return TA_OK;
+  if (n_tokens < 1) return ta::fail(TA_ERR_INVALID_ARGUMENT, "n_tokens %lld < 1", (long long)n_tokens);
+  if (!(w->eps >= 0.f)) return ta::fail(TA_ERR_INVALID_ARGUMENT, "eps must be >= 0");
+  const void* ptrs[] = {hidden, readout_tok, w->norm_w, w->w_gate_up, w->w_down, workspace, h_out};
+  const char* names[] = {"hidden", "readout_tok", "norm_w", "w_gate_up", "w_down", "workspace", "h_out"};
+  for (int i = 0; i < 7; ++i) {
+    if (!ptrs[i]) return ta::fail(TA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!ta::aligned16(ptrs[i]))
+      return ta::fail(TA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+  }
+  const ta::ReadoutLayout l = ta::readout_layout(n_readout, w->d_model, w->d_ff);
+  if (workspace_bytes < l.total)
+    return ta::fail(TA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, l.total);
+  unsigned char* ws = (unsigned char*)workspace;
+  ta::ReadoutArgs a;
+  a.hidden = hidden;
+  a.n_tokens = n_tokens;
+  a.readout_tok = readout_tok;
+  a.norm_w = w->norm_w;
+  a.w_gate_up = w->w_gate_up;
+  a.w_down = w->w_down;
+  a.xn = ws + l.xn;
+  a.act = ws + l.act;
+  a.partial = (float*)(ws + l.partial);
+  a.h_out = h_out;
+  a.n_rows = n_readout;
+  a.d_model = w->d_model;
+  a.d_ff = w->d_ff;
+  a.splits = l.splits;
+  a.eps = w->eps;
+  hipError_t e = ta::launch_readout_mlp(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return ta::hip_fail(e, "readout MLP launch");
+  return TA_OK;
+}
+
+ta_status readout_pack_gate_up(const void* w_gate, const void* w_up, int32_t d_ff, int32_t d_model,
+                               void* w_gate_up, void* hip_stream) {
+  ta::clear_error();
+  ta_status st = ta::check_mlp_shape(0, d_model, d_ff);
+  if (st != TA_OK) return st;
+  const void* ptrs[] = {w_gate, w_up, w_gate_up};
+  const char* names[] = {"w_gate", "w_up", "w_gate_up"};
+  for (int i = 0; i < 3; ++i) {
+    if (!ptrs[i]) return ta::fail(TA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!ta::aligned16(ptrs[i]))
+      return ta::fail(TA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+  }
+  hipError_t e = ta::launch_gate_up_pack(w_gate, w_up, d_ff, d_model, w_gate_up, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return ta::hip_fail(e, "gate/up pack launch");
+  return TA_OK;
+}
+
+ta_status letter_logits(const void* h, int32_t n_readout, int32_t d_model, const void* final_norm_w,
+                        float eps, const void* lm_head, int32_t vocab, const int32_t* letter_ids,
+                        const int32_t* n_letters, int32_t ld, float* logits, void* hip_stream) {
+  ta::clear_error();
+  if (n_readout < 0) return ta::fail(TA_ERR_INVALID_ARGUMENT, "n_readout %d < 0", n_readout);
+  if (d_model < 8 || d_model > ta::kReadoutMaxModel || d_model % 8)
+    return ta::fail(TA_ERR_LIMIT, "d_model %d is not a multiple of 8 in [8, %d]", d_model,
+                    ta::kReadoutMaxModel);
+  if (ld < 1 || ld > 255) return ta::fail(TA_ERR_INVALID_ARGUMENT, "ld %d not in [1, 255]", ld);
+  if (vocab < 1) return ta::fail(TA_ERR_INVALID_ARGUMENT, "vocab %d < 1", vocab);
+  if (!(eps >= 0.f)) return ta::fail(TA_ERR_INVALID_ARGUMENT, "eps must be >= 0");
+  if (n_readout == 0) return TA_OK;
+  const void* ptrs[] = {h, final_norm_w, lm_head};
+  const char* names[] = {"h", "final_norm_w", "lm_head"};
+  for (int i = 0; i < 3; ++i) {
+    if (!ptrs[i]) return ta::fail(TA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!ta::aligned16(ptrs[i]))
+      return ta::fail(TA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+  }
+  if (!letter_ids || !n_letters || !logits) return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL argument");
+  ta::LetterArgs a;
+  a.h = h;
+  a.norm_w = final_norm_w;
+  a.lm_head = lm_head;
+  a.letter_ids = letter_ids;
+  a.n_letters = n_letters;
+  a.logits = logits;
+  a.n_rows = n_readout;
+  a.d_model = d_model;
+  a.vocab = vocab;
+  a.ld = ld;
+  a.eps = eps;
+  hipError_t e = ta::launch_letter_logits(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return ta::hip_fail(e, "letter logits launch");
+  return TA_OK;
+}
+
+}  // extern "C"

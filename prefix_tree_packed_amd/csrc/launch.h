@@ -44,6 +44,34 @@ struct RopeArgs {
   bool interleaved;
 };
 hipError_t launch_rope_cache_write(const RopeArgs& a, hipStream_t st);
+struct ReadoutArgs {
+  const void* hidden;       // f16 [n_tokens, d_model]
+  long long n_tokens;
+  const void* readout_tok;  // int32 [n_rows]
+  const void* norm_w;       // f16 [d_model]
+  const void* w_gate_up;    // f16 [2 d_ff, d_model], gate/up interleaved in 8-row blocks
+  const void* w_down;       // f16 [d_model, d_ff]
+  void* xn;                 // f16 [n_rows, d_model] workspace
+  void* act;                // f16 [n_rows, d_ff] workspace
+  float* partial;           // f32 [splits, n_rows, d_model] workspace
+  void* h_out;              // f16 [n_rows, d_model]
+  int n_rows, d_model, d_ff, splits;
+  float eps;
+};
+hipError_t launch_readout_mlp(const ReadoutArgs& a, hipStream_t st);
+hipError_t launch_gate_up_pack(const void* w_gate, const void* w_up, int d_ff, int d_model, void* out,
+                               hipStream_t st);
+struct LetterArgs {
+  const void* h;          // f16 [n_rows, d_model]
+  const void* norm_w;     // f16 [d_model]
+  const void* lm_head;    // f16 [vocab, d_model]
+  const void* letter_ids; // int32 [n_rows, ld]
+  const void* n_letters;  // int32 [n_rows]
+  float* logits;          // f32 [n_rows, ld]
+  int n_rows, d_model, vocab, ld;
+  float eps;
+};
+hipError_t launch_letter_logits(const LetterArgs& a, hipStream_t st);
 hipError_t launch_decision(const float* logits, int n_rows, int ld, const int* row1, const int* row2,
                            const int* n_letters, const float* T, int n_dec, float* p_avg,
                            float* p_cal, hipStream_t st);
