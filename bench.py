@@ -15,7 +15,10 @@ Prints one JSON line. `value` is useful tree-attention TFLOP/s over the whole
 step (useful FLOPs = 4 * head_dim * q_heads * sum over query tokens of the
 keys each may see); `roofline` is the attention kernel alone, timed with HIP
 events on the launch stream; `cpu_baseline` is the float64 CPU oracle on a
-bounded sample of the same workload (rank 0, one GPU only).
+bounded sample of the same workload (rank 0, one GPU only). `readout` times
+the readout-only last layer (MLP block at the leaf readout rows, letter
+logits) on the Llama shape matching the workload's heads, against HBM
+bandwidth (it streams the MLP weights once); it is not part of the step.
 """
 from __future__ import annotations
 
@@ -82,6 +85,8 @@ def parse():
     ap.add_argument("--rope", choices=["half", "interleaved"], default=None,
                     help="rotate Q and K at the tokens' prompt positions in the cache write "
                          "(fused rotary + cache write) before attention")
+    ap.add_argument("--no-readout", action="store_true",
+                    help="skip timing the readout-only last layer (MLP block and letter logits)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain 256 MiB device copy (known bytes) so "
                          "profiler byte counters can be scaled against it")
@@ -263,6 +268,9 @@ def main():
     for x in fw:
         assert torch.isfinite(x["o"].float()).all().item(), "non-finite attention output"
 
+    if not args.no_readout:
+        out["readout"] = bench_readout(args, wl, plans, dev, stream)
+
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -274,6 +282,74 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, infos, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+# Llama shapes by query heads (8B: 32 heads, 70B: 64); the tiny workload gets a
+# small model of its own width
+READOUT_SHAPES = {32: ("llama-8b", 4096, 14336, 128256), 64: ("llama-70b", 8192, 28672, 128256)}
+
+
+def bench_readout(args, wl, plans, dev, stream):
+    """The readout-only last layer (readout_mlp + letter_logits) at the last
+    forward's leaf readout tokens, on the Llama shape matching the workload's
+    heads, with random weights. HBM-bound: the MLP weights are read once."""
+    import torch
+    import prefix_tree_packed_amd as P
+    name, dm, ff, vocab = READOUT_SHAPES.get(wl.hq, ("small", 256, 768, 4096))
+    plan = plans[-1]
+    readout = P.tree_attn_plan_export(plan)["leaf_readout_tok"]
+    n, n_tok = len(readout), plan.info["num_q_tokens"]
+    d = wl.decisions
+    ld = int(d.logits.shape[1])
+    nl = np.full(n, min(4, ld), np.int32)       # each decision's rows get its letter count
+    for i in range(d.n_dec):
+        for r in (int(d.row1[i]), int(d.row2[i])):
+            if r < n:
+                nl[r] = d.n_letters[i]
+    assert ld <= 8, "the workloads use at most 8 letters"
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    hidden = torch.randn((n_tok, dm), device=dev, generator=g).half()
+    norm_w = (1 + 0.1 * torch.randn(dm, device=dev, generator=g)).half()
+    w_gate_up = (torch.randn((2 * ff, dm), device=dev, generator=g) / dm ** 0.5).half()
+    w_down = (torch.randn((dm, ff), device=dev, generator=g) / ff ** 0.5).half()
+    final_w = (1 + 0.1 * torch.randn(dm, device=dev, generator=g)).half()
+    letters = torch.randint(0, vocab, (8,), device=dev, generator=g, dtype=torch.int32)
+    lm_head = torch.zeros((vocab, dm), dtype=torch.float16, device=dev)
+    lm_head[letters.long()] = (2 * torch.randn((8, dm), device=dev, generator=g) / dm ** 0.5).half()
+    ids = letters[:ld].repeat(n, 1).contiguous()
+    tok = torch.from_numpy(readout).to(dev)
+    n_letters = torch.from_numpy(nl).to(dev)
+    h_out = torch.empty((n, dm), dtype=torch.float16, device=dev)
+    logits = torch.empty((n, ld), dtype=torch.float32, device=dev)
+    ws = torch.empty(P.readout_mlp_workspace_size(n, dm, ff), dtype=torch.uint8, device=dev)
+
+    def run():
+        P.readout_mlp(hidden, tok, norm_w, w_gate_up, w_down, h_out, workspace=ws, stream=stream)
+        P.letter_logits(h_out, final_w, lm_head, ids, n_letters, logits, stream=stream)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    assert torch.isfinite(logits).all().item(), "non-finite letter logits"
+    # algorithmic bytes: the three weight matrices once, the readout rows in and
+    # out, the letters' head rows, the logits
+    weight_bytes = 3 * dm * ff * 2
+    nbytes = weight_bytes + n * dm * 2 * 2 + int(nl.sum()) * dm * 2 + n * ld * 4
+    gbps = nbytes / (us * 1e-6) / 1e9
+    del hidden, w_gate_up, w_down, lm_head
+    torch.cuda.empty_cache()
+    return {"kernels": "readout_norm, mlp_mfma (gate/up, down), readout_finish, letter_logits",
+            "model": name, "d_model": dm, "d_ff": ff, "readout_rows": n, "letters": int(nl.sum()),
+            "bound": "hbm", "us": round(us, 2), "bytes": nbytes, "achieved_gbps": round(gbps, 1),
+            "peak_gbps": PEAK_HBM_GBS, "frac": round(gbps / PEAK_HBM_GBS, 4)}
 
 
 def algorithmic_bytes(plan, wl, out_dtype):

@@ -122,7 +122,7 @@ readout_norm_kernel(const _Float16* __restrict__ hidden, long long n_tokens,
 }
 
 // One workgroup: 64 weight rows, 16 per wave (one MFMA A fragment), against
-// all activation rows (passes of MF*16 rows, the B fragments), over the K range
+// one pass of MF*16 activation rows (the B fragments), over the K range
 // [split * k_len, (split + 1) * k_len). Every output is one wave's MFMA chain
 // over that range in K order.
 //   GATE_UP: w0 is the interleaved gate/up matrix (16-row blocks: gate rows
@@ -147,34 +147,45 @@ constexpr int kRowB = kSlice * 2 + 16;    // LDS row stride in bytes (padded: co
 template <int MF>
 constexpr size_t mlp_lds_bytes() { return 2 * (size_t)MF * 16 * kRowB; }
 
-template <int MF, bool GATE_UP>
-__global__ void __launch_bounds__(kThreads, 2)
+template <int MF, bool GATE_UP, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64)
 mlp_mfma_kernel(const _Float16* __restrict__ x, int ldx,  // activations [n_rows, ldx]
                 const _Float16* __restrict__ w0, int ldw,
-                int n_rows, int k_len, int splits, _Float16* __restrict__ act, int ld_act,
-                float* __restrict__ partial, int ld_part) {
+                int n_rows, int k_len, int splits, int units, _Float16* __restrict__ act,
+                int ld_act, float* __restrict__ partial, int ld_part) {
   __shared__ __attribute__((aligned(16))) unsigned char xs[mlp_lds_bytes<MF>()];  // [2][MF*16][kRowB]
   constexpr int ROWS = MF * 16;
-  constexpr int XCH = ROWS * (kSlice / 8) / kThreads;  // 16-byte chunks per thread per stage
+  constexpr int NT = WAVES * 64;
+  constexpr int WROWS = WAVES * 16;                // weight rows per workgroup
+  constexpr int XCH = ROWS * (kSlice / 8) / NT;    // 16-byte chunks per thread per stage
+  static_assert(XCH >= 1 && ROWS * (kSlice / 8) % NT == 0, "activation stage split");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int split = blockIdx.x % splits;
-  const int j0 = (blockIdx.x / splits) * (GATE_UP ? 32 : 64);
+  // A unit is (weight-row block, K split); each of its row passes is a
+  // workgroup of its own. Workgroups of one unit are 8 apart in launch order:
+  // on the same XCD (workgroups go round-robin over the 8), started together,
+  // so a weight tile streams from HBM once and its other passes hit L2.
+  const int passes = gridDim.x / ((units + 7) / 8 * 8);
+  const int unit = blockIdx.x / (8 * passes) * 8 + blockIdx.x % 8;
+  const int m0 = (blockIdx.x / 8) % passes * ROWS;
+  if (unit >= units) return;  // padding of the last group of 8 units
+  const int split = unit % splits;
+  const int j0 = (unit / splits) * (GATE_UP ? WROWS / 2 : WROWS);
   const int kb = split * k_len;
   const int nstages = k_len / kSlice;
   const int nsteps = nstages * kSteps;
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
 
-  // 64 consecutive weight rows per workgroup, 16 per wave
-  const _Float16* wp = w0 + (size_t)(blockIdx.x / splits * 64 + 16 * wave + r16) * ldw + kb + kq;
+  // WROWS consecutive weight rows per workgroup, 16 per wave
+  const _Float16* wp = w0 + (size_t)(unit / splits * WROWS + 16 * wave + r16) * ldw + kb + kq;
 
-  for (int m0 = 0; m0 < n_rows; m0 += ROWS) {
+  {
     // activation chunks this thread stages: chunk q = tid + i*256 -> row q / 32, 16 B column q % 32
     const _Float16* xsrc[XCH];
     int xdst[XCH];
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
-      const int q = threadIdx.x + i * kThreads;
+      const int q = threadIdx.x + i * NT;
       const int row = q >> 5, cc = q & 31;
       xsrc[i] = x + (size_t)min(m0 + row, n_rows - 1) * ldx + kb + cc * 8;
       xdst[i] = row * kRowB + cc * 16;
@@ -203,7 +214,6 @@ mlp_mfma_kernel(const _Float16* __restrict__ x, int ldx,  // activations [n_rows
 #pragma unroll
     for (int mf = 0; mf < MF; ++mf) acc[mf] = f4{0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();  // the previous pass is done reading the stage buffers
     xload(0, 0);
     xload(1, min(1, nstages - 1));
 #pragma unroll
@@ -362,12 +372,19 @@ letter_logits_kernel(const _Float16* __restrict__ h, int dm, const _Float16* __r
   }
 }
 
+constexpr int kMlpWaves = 4;  // waves (16 weight rows each) per workgroup
+
 template <int MF, bool GU>
 hipError_t launch_mlp(const _Float16* x, int ldx, const _Float16* w0, int ldw,
                       int n_rows, int k_len, int splits, int n_col_blocks, _Float16* act,
                       int ld_act, float* partial, int ld_part, hipStream_t st) {
-  hipLaunchKernelGGL((mlp_mfma_kernel<MF, GU>), dim3(n_col_blocks * splits), dim3(kThreads), 0, st,
-                     x, ldx, w0, ldw, n_rows, k_len, splits, act, ld_act, partial, ld_part);
+  const int units = n_col_blocks * splits;
+  const int passes = (n_rows + MF * 16 - 1) / (MF * 16);
+  const long long grid = (long long)(units + 7) / 8 * 8 * passes;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((mlp_mfma_kernel<MF, GU, kMlpWaves>), dim3((unsigned)grid),
+                     dim3(kMlpWaves * 64), 0, st,
+                     x, ldx, w0, ldw, n_rows, k_len, splits, units, act, ld_act, partial, ld_part);
   return hipGetLastError();
 }
 
@@ -420,11 +437,11 @@ hipError_t launch_readout_mlp(const ReadoutArgs& a, hipStream_t st) {
                      (const int*)a.readout_tok, (const _Float16*)a.norm_w, dm, a.eps, xn);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_mlp_rows<true>(xn, dm, (const _Float16*)a.w_gate_up, dm, n, dm, 1, ff / 32, act, ff,
-                            nullptr, 0, st);
+  e = launch_mlp_rows<true>(xn, dm, (const _Float16*)a.w_gate_up, dm, n, dm, 1, ff / (8 * kMlpWaves),
+                            act, ff, nullptr, 0, st);
   if (e != hipSuccess) return e;
   e = launch_mlp_rows<false>(act, ff, (const _Float16*)a.w_down, ff, n, ff / a.splits,
-                             a.splits, dm / 64, nullptr, 0, a.partial, dm, st);
+                             a.splits, dm / (16 * kMlpWaves), nullptr, 0, a.partial, dm, st);
   if (e != hipSuccess) return e;
   const long long units = (long long)n * (dm / 8);
   hipLaunchKernelGGL(readout_finish_kernel, dim3((unsigned)((units + kThreads - 1) / kThreads)),
