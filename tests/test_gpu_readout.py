@@ -288,3 +288,43 @@ def test_argument_errors(P):
         P.letter_logits(h_out, d["norm_w"], _dev(inp.lm_head()),
                         torch.zeros((2, 300), dtype=torch.int32, device="cuda"),
                         torch.full((2,), 3, dtype=torch.int32, device="cuda"), lg)
+
+
+def test_letter_logits_narrow_rows(P):
+    """letter_logits alone at a width that is a multiple of 8 but not of 256,
+    one-letter rows and ld 1 .. 3, against the oracle within the stage bound."""
+    rng = np.random.default_rng(12)
+    dm, vocab = 264, 40
+    h = (rng.standard_normal((5, dm)) * 3).astype(np.float16)
+    w = (1 + 0.1 * rng.standard_normal(dm)).astype(np.float16)
+    head = (rng.standard_normal((vocab, dm)) / math.sqrt(dm)).astype(np.float16)
+    for ld in (1, 3):
+        ids = rng.integers(0, vocab, (5, ld)).astype(np.int32)
+        nl = np.minimum(rng.integers(1, 4, 5), ld).astype(np.int32)
+        lg = torch.empty((5, ld), dtype=torch.float32, device="cuda")
+        P.letter_logits(_dev(h), _dev(w), _dev(head), _dev(ids), _dev(nl), lg, eps=1e-5)
+        torch.cuda.synchronize()
+        got = lg.cpu().numpy().astype(np.float64)
+        y = R.rms_norm(h.astype(np.float64), w.astype(np.float64), 1e-5)
+        t = 2.0 ** -18 * np.abs(y)
+        y16 = R.rn16(y)
+        wid = np.maximum(np.abs(R.rn16(y + t) - y16), np.abs(y16 - R.rn16(y - t)))
+        for r in range(5):
+            rows = head[ids[r, :nl[r]]].astype(np.float64)
+            tol = np.abs(rows) @ wid[r] + (dm / 16 + 16) * U * (np.abs(rows) @ np.abs(y16[r]))
+            assert np.all(np.abs(got[r, :nl[r]] - rows @ y16[r]) <= tol)
+            assert np.all(got[r, nl[r]:] == 0)
+
+
+def test_no_readout_rows(P):
+    """n_readout = 0 launches nothing and leaves the outputs alone."""
+    inp = WR.draw(4, 8, [], 256, 512, vocab=16, letters=2, ld=2)
+    w_gu = P.readout_pack_gate_up(_dev(inp.w_gate), _dev(inp.w_up))
+    h_out = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    P.readout_mlp(_dev(inp.hidden), torch.empty(0, dtype=torch.int32, device="cuda"), _dev(inp.norm_w), w_gu,
+                  _dev(inp.w_down), h_out)
+    lg = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    P.letter_logits(h_out, _dev(inp.final_norm_w), _dev(inp.lm_head()),
+                    torch.empty((0, 2), dtype=torch.int32, device="cuda"),
+                    torch.empty(0, dtype=torch.int32, device="cuda"), lg)
+    torch.cuda.synchronize()
