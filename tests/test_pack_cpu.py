@@ -174,3 +174,4 @@ def test_nested_prompts_depth_limit(lib, order, max_depth):
                 P.tree_pack(prompts, pp, max_depth=max_depth)
             continue
         _check_same(P.tree_pack(prompts, pp, max_depth=max_depth), prompts, pp, max_depth=max_depth)
+
