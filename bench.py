@@ -19,6 +19,11 @@ bounded sample of the same workload (rank 0, one GPU only). `readout` times
 the readout-only last layer (MLP block at the leaf readout rows, letter
 logits) on the Llama shape matching the workload's heads, against HBM
 bandwidth (it streams the MLP weights once); it is not part of the step.
+`mfma_attainable` is the rate a register-only MFMA loop reaches on this device
+(the shader clock under load is below the published peak's 2.4 GHz), reported
+beside the published peak; `attention_ms_p10_p50_p90` spreads the timed
+launches; `roofline.per_launch.algorithmic_gbps` and `kv_stream_gbps_per_forward`
+give the byte rates (the bound that matters for short-block workloads).
 """
 from __future__ import annotations
 
@@ -85,6 +90,8 @@ def parse():
     ap.add_argument("--rope", choices=["half", "interleaved"], default=None,
                     help="rotate Q and K at the tokens' prompt positions in the cache write "
                          "(fused rotary + cache write) before attention")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip measuring the MFMA rate the device reaches (register-only loop)")
     ap.add_argument("--no-readout", action="store_true",
                     help="skip timing the readout-only last layer (MLP block and letter logits)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -207,7 +214,10 @@ def main():
             b += 2 * t * wl.hq * wl.d * 2 + t * (wl.d // 2) * 2 * 4
         write_bytes.append(b)
     write_gbps = sum(write_bytes) / (write_ms.sum() * 1e-3) / 1e9
+    # K and V of every row-space key a forward's queries may see, read once
+    kv_bytes = [2 * inf["num_kv_tokens"] * wl.hkv * wl.d * 2 for inf in infos]
 
+    alg_bytes_k = algorithmic_bytes(plans[k], wl, args.out_dtype)
     out = {
         "metric": "useful tree-attention TFLOP/s (packed tokens/s and % of f16 MFMA peak alongside)",
         "value": round(value, 3),
@@ -225,6 +235,9 @@ def main():
         "pct_mfma_peak": round(100 * value / PEAK_F16_TFLOPS, 2),
         "attention_only_tflops": round(attn_total_tflops, 3),
         "attention_ms_per_forward": [round(float(x), 5) for x in attn_ms_mean],
+        "attention_ms_p10_p50_p90": [[round(float(np.percentile(attn_ms[:, j], q)), 5) for q in (10, 50, 90)]
+                                     for j in range(n_fw)],
+        "kv_stream_gbps_per_forward": [round(kv / (t * 1e-3) / 1e9, 1) for kv, t in zip(kv_bytes, attn_ms_mean)],
         "cache_write": {"kernel": "rope_cache_write_kernel" if args.rope else "cache_write_kernel",
                         "bound": "hbm", "us_per_forward": [round(float(x) * 1e3, 2) for x in write_ms],
                         "bytes_per_forward": write_bytes, "achieved_gbps": round(write_gbps, 1),
@@ -253,7 +266,8 @@ def main():
             "traffic": None,
             "per_launch": {"useful_flop": useful_flops[k], "avg_ms": round(float(attn_ms_mean[k]), 5),
                            "forward_index": k,
-                           "algorithmic_bytes": algorithmic_bytes(plans[k], wl, args.out_dtype)},
+                           "algorithmic_bytes": alg_bytes_k,
+                           "algorithmic_gbps": round(alg_bytes_k / (attn_ms_mean[k] * 1e-3) / 1e9, 1)},
         },
     }
 
@@ -270,6 +284,10 @@ def main():
 
     if not args.no_readout:
         out["readout"] = bench_readout(args, wl, plans, dev, stream)
+    if not args.no_mfma_probe:
+        probe = mfma_attainable(dev, stream)
+        probe["attention_pct_of_attainable"] = round(100 * achieved / probe["tflops"], 2)
+        out["mfma_attainable"] = probe
 
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
@@ -282,6 +300,31 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, infos, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def mfma_attainable(dev, stream):
+    """The MFMA rate the device reaches on a register-only loop (4 workgroups
+    of 4 waves per CU, 8 independent accumulator chains per wave)."""
+    import torch
+    import prefix_tree_packed_amd as P
+    n_wg = 4 * torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+    iters = 2000
+    for _ in range(2):
+        flops = P.tree_attn_mfma_peak_probe(n_wg, iters, out, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    reps = 10
+    for _ in range(reps):
+        P.tree_attn_mfma_peak_probe(n_wg, iters, out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"kernel": "mfma_peak_kernel (v_mfma_f32_16x16x32_f16, register operands only)",
+            "tflops": round(tflops, 1), "pct_of_published_peak": round(100 * tflops / PEAK_F16_TFLOPS, 2),
+            "workgroups": n_wg, "ms": round(ms, 4)}
 
 
 # Llama shapes by query heads (8B: 32 heads, 70B: 64); the tiny workload gets a

@@ -497,6 +497,19 @@ ta_status tree_request_cost(const int32_t* tokens, const int64_t* prompt_indptr,
  */
 ta_status tree_form_batches(const int64_t* costs, int32_t n, int64_t limit, int32_t* batch);
 
+/*
+ * Measurement helper (no page defines it): the MFMA rate the device reaches in
+ * practice, as a second reference beside the published dense f16 peak. Runs
+ * n_wg workgroups of 4 waves; each wave issues `iters` rounds of 8 independent
+ * v_mfma_f32_16x16x32_f16 on register operands (no memory traffic) and each
+ * thread writes one float to out [n_wg * 256] f32 device. *flops receives the
+ * FLOPs of the launch; time it with events on the same stream.
+ * Errors: TA_ERR_INVALID_ARGUMENT (n_wg outside [1, 65536], iters < 1, NULL),
+ * TA_ERR_HIP.
+ */
+ta_status tree_attn_mfma_peak_probe(int32_t n_wg, int32_t iters, float* out, int64_t* flops,
+                                    void* hip_stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* tree_attn_last_error(void);
 

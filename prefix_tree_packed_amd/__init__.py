@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     tree_attn_forward_cached,
     tree_attn_forward_chunked,
     tree_attn_last_error,
+    tree_attn_mfma_peak_probe,
     tree_attn_plan,
     tree_attn_plan_destroy,
     tree_attn_plan_export,

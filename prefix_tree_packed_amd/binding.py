@@ -30,7 +30,7 @@ EXPORTED = ("tree_attn_plan", "tree_attn_plan_info", "tree_attn_plan_upload",
             "tree_attn_forward_cached",
             "tree_pack", "tree_pack_info", "tree_pack_export", "tree_pack_destroy",
             "tree_request_cost", "tree_form_batches", "readout_mlp_workspace_size", "readout_mlp", "readout_pack_gate_up",
-            "letter_logits", "decision_readout", "tree_attn_last_error")
+            "letter_logits", "decision_readout", "tree_attn_mfma_peak_probe", "tree_attn_last_error")
 
 
 class TreeAttnError(RuntimeError):
@@ -121,6 +121,7 @@ def load_library(path: str = LIB_PATH):
     lib.readout_mlp_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.readout_mlp.argtypes = [vp, i64, vp, i32, ctypes.POINTER(_MlpWeights), vp, ctypes.c_size_t, vp, vp]
     lib.readout_pack_gate_up.argtypes = [vp, vp, i32, i32, vp, vp]
+    lib.tree_attn_mfma_peak_probe.argtypes = [i32, i32, vp, ctypes.POINTER(ctypes.c_int64), vp]
     lib.letter_logits.argtypes = [vp, i32, i32, vp, ctypes.c_float, vp, i32, vp, vp, i32, vp, vp]
     for name in EXPORTED[:-1]:
         getattr(lib, name).restype = ctypes.c_int
@@ -491,6 +492,17 @@ def letter_logits(h, final_norm_w, lm_head, letter_ids, n_letters, logits, eps: 
     _check(load_library().letter_logits(_vp(h), int(n), int(dm), _vp(final_norm_w), float(eps),
                                         _vp(lm_head), int(vocab), _vp(letter_ids), _vp(n_letters),
                                         int(ld), _vp(logits), _stream_handle(stream)))
+
+
+def tree_attn_mfma_peak_probe(n_wg: int, iters: int, out, stream=None) -> int:
+    """Launch the register-only MFMA probe (out: float32 GPU tensor of
+    n_wg * 256 entries); returns the FLOPs it performs."""
+    import torch
+    _expect(out, "out", (n_wg * 256,), torch.float32)
+    flops = ctypes.c_int64()
+    _check(load_library().tree_attn_mfma_peak_probe(int(n_wg), int(iters), _vp(out), ctypes.byref(flops),
+                                                    _stream_handle(stream)))
+    return int(flops.value)
 
 
 # ---------------------------------------------------------------------------

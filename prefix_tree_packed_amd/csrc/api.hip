@@ -363,4 +363,16 @@ ta_status letter_logits(const void* h, int32_t n_readout, int32_t d_model, const
   return TA_OK;
 }
 
+ta_status tree_attn_mfma_peak_probe(int32_t n_wg, int32_t iters, float* out, int64_t* flops,
+                                    void* hip_stream) {
+  ta::clear_error();
+  if (n_wg < 1 || n_wg > 65536 || iters < 1)
+    return ta::fail(TA_ERR_INVALID_ARGUMENT, "n_wg %d or iters %d out of range", n_wg, iters);
+  if (!out || !flops) return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL argument");
+  *flops = ta::mfma_peak_flops(n_wg, iters);
+  hipError_t e = ta::launch_mfma_peak(n_wg, iters, out, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return ta::hip_fail(e, "MFMA probe launch");
+  return TA_OK;
+}
+
 }  // extern "C"

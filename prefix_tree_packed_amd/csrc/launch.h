@@ -72,6 +72,8 @@ struct LetterArgs {
   float eps;
 };
 hipError_t launch_letter_logits(const LetterArgs& a, hipStream_t st);
+hipError_t launch_mfma_peak(int n_wg, int iters, float* out, hipStream_t st);
+long long mfma_peak_flops(int n_wg, int iters);
 hipError_t launch_decision(const float* logits, int n_rows, int ld, const int* row1, const int* row2,
                            const int* n_letters, const float* T, int n_dec, float* p_avg,
                            float* p_cal, hipStream_t st);

@@ -1,0 +1,51 @@
+// Measurement helper: the MFMA rate this device reaches in practice.
+//
+// No page defines it; it gives the measured attention rate a second reference
+// beside the published dense f16 peak (the shader clock under load sits below
+// the 2.4 GHz that figure assumes). Every wave runs independent chains of
+// v_mfma_f32_16x16x32_f16 on register operands only (no memory traffic in the
+// loop), enough chains that each MFMA's latency is hidden behind the others.
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+
+namespace ta {
+
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChains = 8;
+
+__global__ void __launch_bounds__(256) mfma_peak_kernel(int iters, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  // operands that depend on the lane so the compiler cannot fold the products
+  const h8 a = h8{} + (_Float16)(1.0f + lane * 1e-3f);
+  const h8 b = h8{} + (_Float16)(1.0f - lane * 1e-3f);
+  f4 acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = f4{0.f, 0.f, 0.f, (float)c};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+}  // namespace
+
+hipError_t launch_mfma_peak(int n_wg, int iters, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3(n_wg), dim3(256), 0, st, iters, out);
+  return hipGetLastError();
+}
+
+long long mfma_peak_flops(int n_wg, int iters) {
+  // waves x iterations x chains x (16 x 16 x 32 x 2) FLOPs
+  return (long long)n_wg * 4 * iters * kChains * 16LL * 16 * 32 * 2;
+}
+
+}  // namespace ta
