@@ -476,6 +476,11 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
       pb[kc][cg][k2 * 4 + r] = (_Float16)__builtin_amdgcn_exp2f(
           __builtin_fmaf(cur[2 * kc + k2][cg][r], scale_log2e, -mrun[cg]));
     };
+    // The wave in its score phase gets issue priority over the other wave on
+    // its SIMD, which is then more often in its P.V phase or between tiles:
+    // measured 1-3% faster than equal priority (and better than favouring the
+    // P.V phase or alternating by wave).
+    __builtin_amdgcn_s_setprio(1);
     kread(0);
     if (NA > 1) kread(1);
 #pragma unroll
@@ -492,6 +497,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
             kf[i], qf[cg][dc], dc == 0 ? f4{0.f, 0.f, 0.f, 0.f} : nxt[ks][cg], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (j + 2 < NB) vread(j + 2);
