@@ -372,33 +372,40 @@ letter_logits_kernel(const _Float16* __restrict__ h, int dm, const _Float16* __r
   }
 }
 
-constexpr int kMlpWaves = 4;  // waves (16 weight rows each) per workgroup
-
-template <int MF, bool GU>
+// Up to 64 activation rows: one pass, 4 waves (64 weight rows) per workgroup.
+// More: passes of 128 rows with 8 waves (128 weight rows) per workgroup, so
+// the weights stream once per 128 rows and the staged activations per thread
+// stay the same (135 KB of LDS: one workgroup per CU). Each pass is a
+// workgroup of its own.
+template <int MF, bool GU, int WAVES>
 hipError_t launch_mlp(const _Float16* x, int ldx, const _Float16* w0, int ldw,
-                      int n_rows, int k_len, int splits, int n_col_blocks, _Float16* act,
+                      int n_rows, int k_len, int splits, int out_cols, _Float16* act,
                       int ld_act, float* partial, int ld_part, hipStream_t st) {
+  const int n_col_blocks = out_cols / (GU ? 8 * WAVES : 16 * WAVES);
   const int units = n_col_blocks * splits;
   const int passes = (n_rows + MF * 16 - 1) / (MF * 16);
   const long long grid = (long long)(units + 7) / 8 * 8 * passes;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mlp_mfma_kernel<MF, GU, kMlpWaves>), dim3((unsigned)grid),
-                     dim3(kMlpWaves * 64), 0, st,
+  hipLaunchKernelGGL((mlp_mfma_kernel<MF, GU, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64), 0, st,
                      x, ldx, w0, ldw, n_rows, k_len, splits, units, act, ld_act, partial, ld_part);
   return hipGetLastError();
 }
 
 template <bool GU>
-hipError_t launch_mlp_rows(const _Float16* x, int ldx, const _Float16* w0, int ldw, int n_rows, int k_len, int splits, int n_col_blocks,
-                           _Float16* act, int ld_act, float* partial, int ld_part, hipStream_t st) {
+hipError_t launch_mlp_rows(const _Float16* x, int ldx, const _Float16* w0, int ldw, int n_rows,
+                           int k_len, int splits, int out_cols, _Float16* act, int ld_act,
+                           float* partial, int ld_part, hipStream_t st) {
   if (n_rows <= 16)
-    return launch_mlp<1, GU>(x, ldx, w0, ldw, n_rows, k_len, splits, n_col_blocks, act, ld_act,
-                             partial, ld_part, st);
+    return launch_mlp<1, GU, 4>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
+                                partial, ld_part, st);
   if (n_rows <= 32)
-    return launch_mlp<2, GU>(x, ldx, w0, ldw, n_rows, k_len, splits, n_col_blocks, act, ld_act,
-                             partial, ld_part, st);
-  return launch_mlp<4, GU>(x, ldx, w0, ldw, n_rows, k_len, splits, n_col_blocks, act, ld_act,
-                           partial, ld_part, st);
+    return launch_mlp<2, GU, 4>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
+                                partial, ld_part, st);
+  if (n_rows <= 64)
+    return launch_mlp<4, GU, 4>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
+                                partial, ld_part, st);
+  return launch_mlp<8, GU, 8>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
+                              partial, ld_part, st);
 }
 
 // w_gate_up[16i + r] = w_gate[8i + r] (r < 8), w_up[8i + r - 8] (r >= 8); one
@@ -437,11 +444,11 @@ hipError_t launch_readout_mlp(const ReadoutArgs& a, hipStream_t st) {
                      (const int*)a.readout_tok, (const _Float16*)a.norm_w, dm, a.eps, xn);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_mlp_rows<true>(xn, dm, (const _Float16*)a.w_gate_up, dm, n, dm, 1, ff / (8 * kMlpWaves),
-                            act, ff, nullptr, 0, st);
+  e = launch_mlp_rows<true>(xn, dm, (const _Float16*)a.w_gate_up, dm, n, dm, 1, ff, act, ff,
+                            nullptr, 0, st);
   if (e != hipSuccess) return e;
-  e = launch_mlp_rows<false>(act, ff, (const _Float16*)a.w_down, ff, n, ff / a.splits,
-                             a.splits, dm / (16 * kMlpWaves), nullptr, 0, a.partial, dm, st);
+  e = launch_mlp_rows<false>(act, ff, (const _Float16*)a.w_down, ff, n, ff / a.splits, a.splits, dm,
+                             nullptr, 0, a.partial, dm, st);
   if (e != hipSuccess) return e;
   const long long units = (long long)n * (dm / 8);
   hipLaunchKernelGGL(readout_finish_kernel, dim3((unsigned)((units + kThreads - 1) / kThreads)),
