@@ -141,7 +141,8 @@ typedef struct {
   int64_t num_segments;    /* entries of the key tiles' segment table (0 unless tiles by
                               prompt position span several blocks)                        */
   int32_t batch_invariant; /* the configuration's flag                                    */
-  int32_t pad0;
+  int32_t mask_words_per_tile; /* 32-bit words of visibility bits per flagged key tile    */
+  int64_t num_mask_words;  /* all of them: (flagged key tiles + 1) * mask_words_per_tile   */
 } ta_plan_info;
 
 /*
@@ -193,11 +194,13 @@ ta_status tree_attn_plan_export(ta_plan_t plan, int32_t* pos_id, int32_t* tok_ro
  *   q_tiles [num_q_tiles * 5]: per query tile (forward index of its first
  *           token, row-space index of its first token, tokens, first key tile,
  *           end key tile)
- *   key_tiles [num_key_tiles * 7]: per key tile (row-space key of slot 0,
+ *   key_tiles [num_key_tiles * 8]: per key tile (row-space key of slot 0,
  *           keys n, 1 if the kernel applies the per-key visibility test else 0,
- *           lo, hi, segment count, first segment): the tile counts for query t
- *           only if lo <= P(t) < hi; with one segment slot s holds key
- *           k0 + s, otherwise segments[first .. first + count) map slots to keys
+ *           lo, hi, segment count, first segment, visibility block): the tile
+ *           counts for query t only if lo <= P(t) < hi; with one segment slot
+ *           s holds key k0 + s, otherwise segments[first .. first + count) map
+ *           slots to keys; a flagged tile's visibility bits are block b of
+ *           tree_attn_plan_masks (unflagged tiles: block 0, all zero)
  *   work [num_work_items]: the work items longest first, each query_tile *
  *           num_kv_heads + kv_head, the KV heads of one tile together
  *   tok_anc [num_kv_tokens * 2]: per row-space token u, (P(u), E(u)): P is
@@ -212,6 +215,24 @@ ta_status tree_attn_plan_export(ta_plan_t plan, int32_t* pos_id, int32_t* tok_ro
  */
 ta_status tree_attn_plan_schedule(ta_plan_t plan, int32_t* q_tiles, int32_t* key_tiles,
                                   int32_t* work, int32_t* tok_anc, int32_t* segments);
+
+/*
+ * Host copy of the visibility bits the kernel applies on flagged key tiles,
+ * for tests: words [num_mask_words], in blocks of mask_words_per_tile (block b
+ * belongs to the key tiles whose visibility block is b). The bits are laid
+ * out for the kernel's lanes: with W waves of NCG column groups (W = 8 and
+ * NCG = 2 at head_dim 128 with 4 or 8 query heads per KV head; otherwise W = 4
+ * and NCG = min(group, 4) at head_dim 64, 2 or 1 at head_dim 128 for 2 or 1
+ * heads) and w = max(1, NCG / 2) words per lane, lane L of wave v holds words
+ * [(64 v + L) w, (64 v + L + 1) w) of the block. Its element
+ * e = (4 ks + r) NCG + cg, bit e % 32 of word e / 32, is set iff key slot
+ * 16 ks + 4 (L / 16) + r is visible to the query token
+ * min(c / group, n_tok - 1) of the tile, c = 16 NCG v + 16 cg + L % 16, i.e.
+ * the slot holds a key (< n), the tile counts for the token (lo <= P(t) < hi)
+ * and P(u) <= P(t) < E(u).
+ * Errors: TA_ERR_INVALID_ARGUMENT (NULL pointer).
+ */
+ta_status tree_attn_plan_masks(ta_plan_t plan, uint32_t* words);
 
 /*
  * Cap the number of persistent workgroups later uploads may launch (0, the

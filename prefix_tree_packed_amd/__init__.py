@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     tree_attn_plan_destroy,
     tree_attn_plan_export,
     tree_attn_plan_info,
+    tree_attn_plan_masks,
     tree_attn_plan_schedule,
     tree_attn_plan_set_max_workgroups,
     tree_attn_plan_upload,

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "TA_OK", 1: "TA_ERR_INVALID_ARGUMENT", 2: "TA_ERR_INVALID_TRE
 TA_F16, TA_F32 = 0, 1
 
 EXPORTED = ("tree_attn_plan", "tree_attn_plan_info", "tree_attn_plan_upload",
-            "tree_attn_plan_export", "tree_attn_plan_schedule", "tree_attn_plan_set_max_workgroups",
+            "tree_attn_plan_export", "tree_attn_plan_schedule", "tree_attn_plan_masks",
+            "tree_attn_plan_set_max_workgroups",
             "tree_attn_plan_workgroups", "tree_attn_plan_destroy", "tree_attn_forward",
             "tree_attn_forward_chunked", "tree_attn_cache_write", "tree_attn_rope_cache_write",
             "tree_attn_forward_cached",
@@ -66,7 +67,7 @@ class _PlanInfo(ctypes.Structure):
                 ("num_masked_key_tiles", ctypes.c_int64), ("q_tile_tokens", ctypes.c_int32),
                 ("one_shot", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
                 ("num_segments", ctypes.c_int64), ("batch_invariant", ctypes.c_int32),
-                ("pad0", ctypes.c_int32)]
+                ("mask_words_per_tile", ctypes.c_int32), ("num_mask_words", ctypes.c_int64)]
 
 
 class _PackInfo(ctypes.Structure):
@@ -101,6 +102,7 @@ def load_library(path: str = LIB_PATH):
     lib.tree_attn_plan_upload.argtypes = [vp, vp, ctypes.c_size_t, vp]
     lib.tree_attn_plan_export.argtypes = [vp, p32, p32, p32, p32, p32, p32]
     lib.tree_attn_plan_schedule.argtypes = [vp, p32, p32, p32, p32, p32]
+    lib.tree_attn_plan_masks.argtypes = [vp, vp]
     lib.tree_attn_plan_set_max_workgroups.argtypes = [vp, i32]
     lib.tree_attn_plan_workgroups.argtypes = [vp, i32, p32, p32]
     lib.tree_attn_plan_destroy.argtypes = [vp]
@@ -244,7 +246,7 @@ def tree_attn_plan_schedule(plan: Plan) -> dict:
     pre-order positions and subtree ends)."""
     info = plan.info
     out = {"q_tiles": np.zeros((info["num_q_tiles"], 5), np.int32),
-           "key_tiles": np.zeros((info["num_key_tiles"], 7), np.int32),
+           "key_tiles": np.zeros((info["num_key_tiles"], 8), np.int32),
            "work": np.zeros(info["num_work_items"], np.int32),
            "tok_anc": np.zeros((info["num_kv_tokens"], 2), np.int32),
            "segments": np.zeros((info["num_segments"], 2), np.int32)}
@@ -254,9 +256,18 @@ def tree_attn_plan_schedule(plan: Plan) -> dict:
     return out
 
 
+def tree_attn_plan_masks(plan: Plan) -> np.ndarray:
+    """Host copy of the visibility bits of the flagged key tiles, reshaped to
+    [blocks, mask_words_per_tile] (uint32)."""
+    info = plan.info
+    out = np.zeros(info["num_mask_words"], np.uint32)
+    _check(load_library().tree_attn_plan_masks(plan.handle, out.ctypes.data_as(ctypes.c_void_p)))
+    return out.reshape(-1, info["mask_words_per_tile"])
+
+
 def key_tile_rows(sch: dict, i: int) -> np.ndarray:
     """Row-space keys of key tile i of an exported schedule, in slot order."""
-    k0, n, _, _, _, nseg, seg = (int(x) for x in sch["key_tiles"][i])
+    k0, n, _, _, _, nseg, seg, _ = (int(x) for x in sch["key_tiles"][i])
     if nseg == 1:
         return np.arange(k0, k0 + n)
     segs = sch["segments"][seg:seg + nseg]

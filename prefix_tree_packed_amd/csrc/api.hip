@@ -41,11 +41,10 @@ static AttnArgs attn_args(ta_plan_t p, const void* q, const void* k, const void*
   a.lse = lse;
   a.qtiles = ws + p->off_qtiles;
   a.ktiles = ws + p->off_ktiles;
-  a.kvis = ws + p->off_kvis;
+  a.mbits = ws + p->off_mbits;
   a.segs = ws + p->off_segs;
   a.wg_ptr = ws + p->off_wg_ptr;
   a.wg_items = ws + p->off_wg_items;
-  a.tok_anc = ws + p->off_anc;
   a.hq = p->cfg.num_q_heads;
   a.hkv = p->cfg.num_kv_heads;
   a.head_dim = p->cfg.head_dim;

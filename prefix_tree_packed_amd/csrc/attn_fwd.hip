@@ -20,10 +20,11 @@
 //   S^T = K Q^T     v_mfma_f32_16x16x32_f16, A = K rows from LDS, B = Q
 //   mask            only on tiles the plan flags: key u is visible to query t
 //                   iff u's block is a proper ancestor of t's block or the
-//                   same block with u <= t, tested as P(u) <= P(t) < E(u) on
-//                   the plan's token pre-order positions P and subtree ends E,
-//                   and the tile counts for t (its [lo, hi) holds P(t): with
-//                   tiles by prompt position a tile belongs to one path)
+//                   same block with u <= t (and the tile counts for t); the
+//                   plan stores that as one bit per score in the lane layout
+//                   of the S^T accumulators, loaded into LDS with the tile,
+//                   and a set bit keeps the score, a clear one makes it -inf
+//                   (two VALU ops per score)
 //   softmax         one running reference max per column (two cross-lane steps
 //                   over the 4 lane groups that share a column), moved only
 //                   when a score exceeds it by 2^8; exp2 with log2(e) folded
@@ -91,6 +92,16 @@ __device__ __forceinline__ float column_max(float x) {
 // receives V[key0 + 4g + j][d0 + i'] for j = 0..3: four consecutive keys of one
 // head-dim column, which is the A-operand layout of the P.V MFMA.
 // ---------------------------------------------------------------------------
+// LDS read-ahead inside the fused block: K fragments are read KPF sub-steps
+// before the S sub-step that uses them, V^T fragments VPF sub-steps before
+// their P.V sub-step.
+#ifndef TA_KPF
+#define TA_KPF 2
+#endif
+#ifndef TA_VPF
+#define TA_VPF 2
+#endif
+
 // LDS stages: a tile's loads are issued three tiles ahead of its P.V product
 // (two ahead of its S product). A power of two.
 constexpr int kStages = 4;
@@ -99,13 +110,13 @@ typedef short s4v __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s4v lds_s4v;
 
-template <int D>
+template <int D, int MW>
 struct DlLds {
   static constexpr int ROWB = D * 2;               // bytes per K/V row
   static constexpr int TILEB = kKeyTile * ROWB;   // bytes per K (or V) tile
   unsigned char k[kStages][TILEB];
   unsigned char v[kStages][TILEB];
-  int2 anc[kStages][kKeyTile];
+  unsigned mbits[kStages][MW];                     // the tile's visibility bits
 };
 
 // 16 bytes per lane from global memory straight into LDS at M0 + 16*lane
@@ -149,24 +160,27 @@ __global__ void __launch_bounds__(WAVES * 64)
 tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                         const _Float16* __restrict__ V, void* __restrict__ Out,
                         float* __restrict__ Lse, const QTile* __restrict__ qtiles,
-                        const KTile* __restrict__ ktiles, const int2* __restrict__ kvis,
+                        const KTile* __restrict__ ktiles, const unsigned* __restrict__ mbits,
                         const Seg* __restrict__ segs,
                         const int* __restrict__ wg_ptr, const int* __restrict__ wg_items,
-                        const int2* __restrict__ tok_anc, int hq, int hkv, int n_q_total,
+                        int hq, int hkv, int n_q_total,
                         float scale_log2e) {
   constexpr int DC = D / 32;
   constexpr int DT = D / 16;
   constexpr int CPW = 16 * NCG;
   constexpr int DCH = D / 8;                       // 16-byte chunks per row
-  constexpr int ROWB = DlLds<D>::ROWB;
+  constexpr int WPL = NCG > 2 ? NCG / 2 : 1;      // visibility words per lane
+  constexpr int MW = WAVES * 64 * WPL;             // visibility words per key tile
+  constexpr int MWB = 64 * WPL * 4;                // visibility bytes loaded per wave
+  constexpr int ROWB = DlLds<D, MW>::ROWB;
   constexpr int RPI = 1024 / ROWB;                 // rows per wave-wide 1 KB load
   constexpr int IPW = kKeyTile / RPI / WAVES;      // loads per wave per K (or V) tile
-  constexpr int ANCB = kKeyTile * 8 / WAVES;       // anc bytes loaded per wave
   constexpr int LOADS = 2 * IPW + 1;               // vector-memory ops per wave per tile
   static_assert(IPW >= 1 && kKeyTile % (RPI * WAVES) == 0, "tile / wave shape");
-  static_assert(ANCB % 16 == 0 && ANCB / 16 <= 64, "anc split");
+  static_assert(MWB % 16 == 0 && MWB / 16 <= 64, "visibility split");
+  static_assert(16 * NCG <= 32 * WPL, "visibility bits per lane");
 
-  __shared__ DlLds<D> lds;
+  __shared__ DlLds<D, MW> lds;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -196,14 +210,10 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   auto issue = [&](int stage, int kvh, const KTile& t) {
     const int nk = t.meta & 0xffff;
     const int nseg = ((t.meta >> kSegShift) & (kMaxSegs - 1)) + 1;
-    // slot 0's row and the first per-key (P, E) entry: k0 itself for a
-    // one-segment tile, else from the header at segs[k0]
-    int k0 = t.k0, anc = t.k0;
-    if (nseg > 1) {
-      const Seg h = segs[t.k0];
-      anc = h.slot0;
-      k0 = h.row0;
-    }
+    // slot 0's row: k0 itself for a one-segment tile, else from the header
+    // at segs[k0]
+    int k0 = t.k0;
+    if (nseg > 1) k0 = segs[t.k0].row0;
     const _Float16* kb = K + (size_t)kvh * D + (size_t)k0 * kv_stride;
     const _Float16* vb = V + (size_t)kvh * D + (size_t)k0 * kv_stride;
     // element offset of each loaded slot's row from slot 0's row: the slot
@@ -234,11 +244,12 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
       lds_dma16(kb + roff[j] + kch[j], lds_addr_of(lds.k[stage] + (wave * IPW + j) * 1024));
       lds_dma16(vb + roff[j] + vch[j], lds_addr_of(lds.v[stage] + (wave * IPW + j) * 1024));
     }
-    // (P, E) of the tile's 64 slots (ANCB bytes per wave; the plan pads
-    // tok_anc so a full tile's worth past any entry is readable)
-    if (lane < ANCB / 16)
-      lds_dma16((const char*)(tok_anc + anc) + wave * ANCB + 16 * lane,
-                lds_addr_of((const char*)lds.anc[stage] + wave * ANCB));
+    // this wave's visibility words of the tile; an unflagged tile needs none,
+    // but one lane still loads 16 bytes of block 0 (all zero, never read) so
+    // that every tile issues the same number of loads per wave
+    if (lane < ((t.meta & kMaskedBit) ? MWB / 16 : 1))
+      lds_dma16((const char*)(mbits + (size_t)t.mblk * MW) + wave * MWB + 16 * lane,
+                lds_addr_of((const char*)lds.mbits[stage] + wave * MWB));
   };
 
   // Load cursor: the workgroup's key tiles as one sequence over its items.
@@ -267,12 +278,10 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   // are recomputed from the tile where needed rather than kept in registers.
   int c_kvh = 0;
   QTile tile;
-  int tpos[NCG];
   h8 qf[NCG][DC];
   auto col_token = [&](int cg, int n_tok) { return min((wave * CPW + cg * 16 + l16) / G, n_tok - 1); };
   auto col_head = [&](int cg, int kvh) { return kvh * G + (wave * CPW + cg * 16 + l16) % G; };
-  // Opens item `pos`: its tile, the columns' pre-order positions and the Q
-  // fragments (loads left in flight).
+  // Opens item `pos`: its tile and the Q fragments (loads left in flight).
   auto open_item = [&](int pos) {
     const int w = wg_items[pos];
     const int qt = w / hkv;
@@ -281,7 +290,6 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
       const int t = col_token(cg, tile.n_tok);
-      tpos[cg] = tok_anc[tile.q_row + t].x;
       const _Float16* qp = Q + ((size_t)(tile.q_fwd + t) * hq + col_head(cg, c_kvh)) * D + 8 * lg;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) qf[cg][dc] = *(const h8*)(qp + 32 * dc);
@@ -313,7 +321,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   const int vbase = vr * ROWB + 8 * (lane & 3);
   const int vsw = v_swizzle<DCH>(vr);
 
-  // Everything issued so far (the first tiles, Q, positions) was in flight
+  // Everything issued so far (the first tiles, Q) was in flight
   // together; waiting for all of it here costs little and leaves the
   // compiler with no outstanding loads to wait for inside the loop, where any
   // wait of its own would also drain the tile being prefetched.
@@ -339,29 +347,24 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     }
   };
 
-  // -inf for keys query t must not see (flagged tiles only): the tile must
-  // count for t (lo <= P(t) < hi; else t's position is taken as -1, which no
-  // key passes) and key u must pass P(u) <= P(t) < E(u)
-  auto apply_mask = [&](int stage, int kt, const KTile& t, f4 (&sacc)[4][NCG]) {
-    const int nk = t.meta & 0xffff;
-    const int2 vis = kvis[kt];
-    int tp[NCG];
+  // -inf for keys a column must not see (flagged tiles only), from the
+  // tile's visibility bits: element (ks, r, cg) is bit (4 ks + r) NCG + cg of
+  // the lane's words; the bit, sign-extended, selects the score or -inf
+  auto apply_mask = [&](int stage, f4 (&sacc)[4][NCG]) {
+    unsigned bits[WPL];
 #pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) tp[cg] = ((vis.x <= tpos[cg]) & (tpos[cg] < vis.y)) ? tpos[cg] : -1;
+    for (int w = 0; w < WPL; ++w) bits[w] = lds.mbits[stage][(wave * 64 + lane) * WPL + w];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kidx = 16 * ks + 4 * lg + r;
-        const int2 an = lds.anc[stage][kidx];
-        const int pu = kidx < nk ? an.x : 0x7fffffff;  // slots past the tile: never
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int cg = 0; cg < NCG; ++cg) {
-          const bool vis = (pu <= tp[cg]) & (tp[cg] < an.y);
-          sacc[ks][cg][r] = vis ? sacc[ks][cg][r] : -__builtin_inff();
+          const int e = (4 * ks + r) * NCG + cg;
+          const unsigned m = (unsigned)((int)(bits[e / 32] << (31 - e % 32)) >> 31);
+          sacc[ks][cg][r] =
+              __uint_as_float((__float_as_uint(sacc[ks][cg][r]) & m) | (0xff800000u & ~m));
         }
-      }
-    }
   };
 
   // Column max of one tile's scores, reduced over the column's four lanes
@@ -443,6 +446,9 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   // keep every live tile resident. (Unrolling by two so the two score buffers
   // swap roles instead of being copied runs out of registers; the copy mostly
   // coalesces away.)
+  constexpr int KPF = TA_KPF;                // K fragments read ahead of their S sub-step
+  constexpr int VPF = TA_VPF;                // V^T fragments read ahead of their P.V sub-step
+  static_assert(KPF >= 1 && VPF >= 1 && VPF <= 4 * DC, "read-ahead distances");
   constexpr int NA = 4 * DC;                 // S sub-steps: one K fragment each
   constexpr int NE = 16 * NCG;               // probabilities per lane per tile
   constexpr int EPS = (NE + NA - 1) / NA;    // of them per S sub-step
@@ -481,13 +487,14 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     // measured 1-3% faster than equal priority (and better than favouring the
     // P.V phase or alternating by wave).
     __builtin_amdgcn_s_setprio(1);
-    kread(0);
-    if (NA > 1) kread(1);
+#pragma unroll
+    for (int i = 0; i < KPF && i < NA; ++i) kread(i);
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      if (i + 2 < NA) kread(i + 2);
-      if (i == NA - 2) vread(0);
-      if (i == NA - 1) vread(1);
+      if (i + KPF < NA) kread(i + KPF);
+#pragma unroll
+      for (int j = 0; j < VPF; ++j)
+        if (i == NA - VPF + j) vread(j);
 #pragma unroll
       for (int e = i * EPS; e < (i + 1) * EPS && e < NE; ++e) prob(e);
       const int ks = i / DC, dc = i % DC;
@@ -500,7 +507,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      if (j + 2 < NB) vread(j + 2);
+      if (j + VPF < NB) vread(j + VPF);
       const int kc = j / DT, dt = j % DT;
       if (dt == 0) {
 #pragma unroll
@@ -562,7 +569,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
 
     const KTile t1 = ktiles[kt + 1];
     if (t1.meta & kMaskedBit) {
-      apply_mask(s1, kt + 1, t1, nxt);
+      apply_mask(s1, nxt);
       float m[NCG];
       tile_max_raw(nxt, m);
 #pragma unroll
@@ -586,7 +593,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     {
       s_product(s, sa);
       const KTile t0 = ktiles[ktb];
-      if (t0.meta & kMaskedBit) apply_mask(s, ktb, t0, sa);
+      if (t0.meta & kMaskedBit) apply_mask(s, sa);
       float mx[NCG];
       tile_max_raw(sa, mx);
       move_reference(mx);
@@ -661,10 +668,10 @@ static hipError_t variant(const AttnArgs* a, hipStream_t st, int* per_cu) {
   if (!a) return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, kernel, WAVES * 64, 0);
   hipLaunchKernelGGL(kernel, dim3(a->n_wg), dim3(WAVES * 64), 0, st, (const _Float16*)a->q,
                      (const _Float16*)a->k, (const _Float16*)a->v, a->o, a->lse,
-                     (const QTile*)a->qtiles, (const KTile*)a->ktiles, (const int2*)a->kvis,
+                     (const QTile*)a->qtiles, (const KTile*)a->ktiles, (const unsigned*)a->mbits,
                      (const Seg*)a->segs,
                      (const int*)a->wg_ptr,
-                     (const int*)a->wg_items, (const int2*)a->tok_anc, a->hq, a->hkv, a->n_q,
+                     (const int*)a->wg_items, a->hq, a->hkv, a->n_q,
                      a->scale_log2e);
   return hipGetLastError();
 }

@@ -40,16 +40,18 @@ struct ta_plan_s {
   // device tables, laid out in `image` at the offsets below (256-byte aligned)
   std::vector<ta::QTile> qtiles;
   std::vector<ta::KTile> ktiles;
-  std::vector<ta::Int2> kvis;       // per key tile: [lo, hi) of the queries it counts for
+  std::vector<ta::Int2> kvis;       // per key tile: [lo, hi) of the queries it counts for (host)
   std::vector<ta::Seg> segs;        // header + segments of each multi-segment key tile
   std::vector<int32_t> work;        // qtile * num_kv_heads + kv_head, launch order
   std::vector<ta::Int2> tok_anc;    // per row-space token: (P, subtree end), see number_blocks;
-                                    // then 64 entries per multi-segment key tile
+                                    // then 64 entries per multi-segment key tile (host)
+  std::vector<uint32_t> mbits;      // visibility bits of the flagged key tiles (layout.h)
+  int mask_words = 0;               // 32-bit words per key tile's block of bits
   std::vector<int32_t> tok_rowpos;  // per forward token: its row-space index
   std::vector<double> item_cost;    // per query tile: weighted key tiles (workgroup packing)
   int64_t n_masked_ktiles = 0;
 
-  size_t off_qtiles = 0, off_ktiles = 0, off_kvis = 0, off_segs = 0, off_work = 0, off_anc = 0,
+  size_t off_qtiles = 0, off_ktiles = 0, off_mbits = 0, off_segs = 0, off_work = 0,
          off_rowpos = 0;
   size_t off_wg_ptr = 0, off_wg_items = 0, off_posid = 0;
   int32_t max_pos_id = -1;          // largest position id of this forward's tokens

@@ -13,11 +13,10 @@ struct AttnArgs {
   float* lse;
   const void* qtiles;
   const void* ktiles;
-  const void* kvis;      // per key tile: [lo, hi) of the queries it counts for
+  const void* mbits;     // visibility bits of the flagged key tiles (layout.h)
   const void* segs;      // headers and segments of multi-segment key tiles
   const void* wg_ptr;    // [n_wg + 1] item ranges of the persistent workgroups
   const void* wg_items;  // work items (query tile * hkv + kv head), per workgroup
-  const void* tok_anc;
   int hq, hkv, head_dim, group, n_q, n_wg;
   float scale_log2e;
   bool out_f32;

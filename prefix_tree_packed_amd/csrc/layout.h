@@ -24,15 +24,16 @@ struct QTile {
 // 16 bits, in bit 16 whether the tile needs the per-element visibility test
 // (some key is not visible to every query of the tile, or the tile is short),
 // and nseg - 1 in bits 17-19. With one segment, slot s holds row-space key
-// k0 + s and the per-key (P, E) entries start at tok_anc[k0]. With several,
-// k0 is an index h into the segment table: segs[h] = {first (P, E) entry, row
-// of slot 0} and segs[h + 1 .. h + nseg] are the segments (Seg below). Kept at
-// 8 bytes so a scalar-cache line holds 8 tiles; the tile's visibility interval
-// lives in a side table read only for flagged tiles: the tile counts for query
-// t only if lo <= P(t) < hi (P: the token pre-order position).
+// k0 + s. With several, k0 is an index h into the segment table: segs[h] =
+// {first (P, E) entry of the tile's slots, row of slot 0} and segs[h + 1 ..
+// h + nseg] are the segments (Seg below). `mblk` is the tile's block of
+// visibility bits (see mask_words_per_lane); unflagged tiles point at block 0, which
+// is all zero and never read.
 struct KTile {
   int32_t k0;
   int32_t meta;
+  int32_t mblk;
+  int32_t pad;
 };
 
 // Segment of a multi-segment key tile: slots [slot0, next segment's slot0)
@@ -75,6 +76,22 @@ inline constexpr int column_groups_for(int group, int head_dim) {
 }
 inline constexpr int q_tile_tokens_for(int group, int head_dim) {
   return waves_for(group, head_dim) * 16 * column_groups_for(group, head_dim) / group;
+}
+
+// Visibility bits of a flagged key tile, one block per tile laid out for the
+// kernel's lanes. Lane L of wave w owns, for each of its column groups cg, the
+// column c = 16 * NCG * w + 16 * cg + L % 16 (query token min(c / group,
+// n_tok - 1) of the tile) and the key slots 16 * ks + 4 * (L / 16) + r, ks and
+// r in 0..3 -- the S^T accumulator elements it holds. Element
+// e = (4 * ks + r) * NCG + cg is bit e % 32 of the lane's word e / 32; a set
+// bit means the key is visible to that query (it counts for it, is a real key
+// of the tile and passes the ancestor-or-own-prefix test). A block holds
+// waves * 64 lanes * words_per_lane 32-bit words, lane-major.
+inline constexpr int mask_words_per_lane(int group, int head_dim) {
+  return column_groups_for(group, head_dim) > 2 ? column_groups_for(group, head_dim) / 2 : 1;
+}
+inline constexpr int mask_words_per_tile(int group, int head_dim) {
+  return waves_for(group, head_dim) * 64 * mask_words_per_lane(group, head_dim);
 }
 
 }  // namespace ta

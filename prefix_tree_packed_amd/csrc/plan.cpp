@@ -15,8 +15,11 @@
 // short leaves from wasting matrix-core lanes). For each tile the keys any of
 // its tokens may see -- the full ranges of its blocks' ancestors plus each own
 // block's prefix up to the tile end -- are merged into disjoint row-space
-// ranges and cut into 64-key tiles. A key tile that every query of the tile
-// sees in full is "unmasked": the kernel skips the visibility test there.
+// ranges, and the keys of those ranges, in row order, are cut into 64-key
+// tiles that run on across range ends (a tile gathers up to kMaxSegs ranges),
+// so only a tile's last key tile is short. A full key tile that every query of
+// the tile sees in full is "unmasked": the kernel skips the visibility test
+// there.
 // Tiles are ordered longest-first so that a plain grid launch schedules them
 // as longest-processing-time-first list scheduling, and the KV heads of a tile
 // are interleaved so that consecutive workgroups (which the dispatcher deals
@@ -86,6 +89,8 @@ struct Builder {
   void token_tables();
   ta_status schedule();
   void position_tiles(const RowView& v, int32_t a, int32_t b);
+  void emit_tile(const Seg* sg, int nseg, int32_t n, bool full, Int2 vis);
+  void mask_bits();
   int32_t block_of(const RowView& r, int32_t i) const;
   bool chunk_full(const RowView& r, int32_t k0, int32_t k1, int32_t a,
                   const std::vector<int32_t>& touched) const;
@@ -293,6 +298,88 @@ bool Builder::chunk_full(const RowView& r, int32_t k0, int32_t k1, int32_t a,
   return true;
 }
 
+// Appends one key tile of n keys in nseg segments (slot0, row-space row0),
+// flagged for the per-key test unless `full`, counting for the queries t with
+// vis.x <= P(t) < vis.y. A tile of several segments gets a header and its own
+// 64 (P, E) entries at the end of tok_anc (slots past n: (0, 0), seen by none).
+void Builder::emit_tile(const Seg* sg, int nseg, int32_t n, bool full, Int2 vis) {
+  KTile kt{};
+  kt.meta = n | (full ? 0 : kMaskedBit) | ((nseg - 1) << kSegShift);
+  if (nseg == 1) {
+    kt.k0 = sg[0].row0;
+  } else {
+    kt.k0 = (int32_t)p->segs.size();
+    p->segs.push_back(Seg{(int32_t)p->tok_anc.size(), sg[0].row0});  // header
+    for (int k = 0; k < nseg; ++k) p->segs.push_back(sg[k]);
+    for (int32_t slot = 0; slot < kKeyTile; ++slot) {
+      Int2 e{0, 0};
+      for (int k = nseg - 1; k >= 0; --k)
+        if (slot < n && slot >= sg[k].slot0) {
+          e = p->tok_anc[sg[k].row0 + (slot - sg[k].slot0)];
+          break;
+        }
+      p->tok_anc.push_back(e);
+    }
+  }
+  if (!full) ++p->n_masked_ktiles;
+  p->ktiles.push_back(kt);
+  p->kvis.push_back(vis);
+}
+
+// Visibility bits of every flagged key tile, in the lane layout of the kernel
+// variant the plan launches (layout.h, mask_words_per_lane). Key u of slot s counts for
+// query t of the tile iff s < n, lo <= P(t) < hi and P(u) <= P(t) < E(u).
+// Block 0 stays zero for the unflagged tiles.
+void Builder::mask_bits() {
+  const int G = p->group, D = p->cfg.head_dim;
+  const int waves = waves_for(G, D), ncg = column_groups_for(G, D);
+  const int wpl = mask_words_per_lane(G, D);
+  const int mw = mask_words_per_tile(G, D);
+  p->mask_words = mw;
+  p->mbits.assign(mw, 0u);
+  std::vector<uint64_t> tokvis;  // per query token of the tile: bit s = slot s visible
+  for (const QTile& q : p->qtiles) {
+    for (int32_t k = q.kt_begin; k < q.kt_end; ++k) {
+      KTile& t = p->ktiles[k];
+      if (!(t.meta & kMaskedBit)) {
+        t.mblk = 0;
+        continue;
+      }
+      const int32_t n = t.meta & 0xffff;
+      const int nseg = ((t.meta >> kSegShift) & (kMaxSegs - 1)) + 1;
+      const Int2* ue = p->tok_anc.data() + (nseg == 1 ? t.k0 : p->segs[t.k0].slot0);
+      const Int2 vis = p->kvis[k];
+      tokvis.assign(q.n_tok, 0);
+      for (int32_t i = 0; i < q.n_tok; ++i) {
+        const int32_t pt = p->tok_anc[q.q_row + i].x;
+        if (pt < vis.x || pt >= vis.y) continue;
+        uint64_t w = 0;
+        for (int32_t s = 0; s < n; ++s)
+          if (ue[s].x <= pt && pt < ue[s].y) w |= uint64_t(1) << s;
+        tokvis[i] = w;
+      }
+      t.mblk = (int32_t)(p->mbits.size() / mw);
+      const size_t base = p->mbits.size();
+      p->mbits.resize(base + mw, 0u);
+      uint32_t* blk = p->mbits.data() + base;
+      for (int w = 0; w < waves; ++w)
+        for (int lane = 0; lane < 64; ++lane) {
+          uint32_t* lw = blk + ((size_t)w * 64 + lane) * wpl;
+          for (int cg = 0; cg < ncg; ++cg) {
+            const int col = 16 * ncg * w + 16 * cg + lane % 16;
+            const uint64_t tv = tokvis[std::min(col / G, q.n_tok - 1)];
+            for (int ks = 0; ks < 4; ++ks)
+              for (int r = 0; r < 4; ++r) {
+                const int slot = 16 * ks + 4 * (lane / 16) + r;
+                const int e = (4 * ks + r) * ncg + cg;
+                if ((tv >> slot) & 1) lw[e / 32] |= 1u << (e % 32);
+              }
+          }
+        }
+    }
+  }
+}
+
 // Key tiles of one query tile (row-local tokens [a, b) of row v) by position in
 // each query's own prompt: for every block B the tile touches and every window
 // j = 0 .. (largest position of B's tokens here) / 64, the window holds the
@@ -346,7 +433,6 @@ void Builder::position_tiles(const RowView& v, int32_t a, int32_t b) {
   });
   for (const Win& w : wins) {
     const int32_t w0 = w.j * kKeyTile;
-    KTile kt{};
     Int2 vis;
     vis.x = tpre[w.owner];
     vis.y = w.full ? tend[w.owner] : tpre[w.owner] + d->block_len[w.owner];
@@ -370,26 +456,7 @@ void Builder::position_tiles(const RowView& v, int32_t a, int32_t b) {
       const int32_t pos = anc_len[B] + (i - start[B]);
       all = vis.x <= pt && pt < vis.y && pos >= w0 + kKeyTile - 1;
     }
-    kt.meta = w.n | (all ? 0 : kMaskedBit) | ((nseg - 1) << kSegShift);
-    if (nseg == 1) {
-      kt.k0 = sg[0].row0;
-    } else {
-      kt.k0 = (int32_t)p->segs.size();
-      p->segs.push_back(Seg{(int32_t)p->tok_anc.size(), sg[0].row0});  // header
-      for (int k = 0; k < nseg; ++k) p->segs.push_back(sg[k]);
-      for (int32_t slot = 0; slot < kKeyTile; ++slot) {
-        Int2 e{0, 0};
-        for (int k = nseg - 1; k >= 0; --k)
-          if (slot < w.n && slot >= sg[k].slot0) {
-            e = p->tok_anc[sg[k].row0 + (slot - sg[k].slot0)];
-            break;
-          }
-        p->tok_anc.push_back(e);
-      }
-    }
-    if (!all) ++p->n_masked_ktiles;
-    p->ktiles.push_back(kt);
-    p->kvis.push_back(vis);
+    emit_tile(sg, nseg, w.n, all, vis);
   }
 }
 
@@ -430,30 +497,40 @@ ta_status Builder::schedule() {
         ranges.push_back({start[B], std::min(start[B] + d->block_len[B], b)});
       }
       std::sort(ranges.begin(), ranges.end());
+      // merge into disjoint ranges, in row order
+      size_t m = 0;
+      for (size_t i = 0; i < ranges.size(); ++i) {
+        if (m > 0 && ranges[i].first <= ranges[m - 1].second)
+          ranges[m - 1].second = std::max(ranges[m - 1].second, ranges[i].second);
+        else
+          ranges[m++] = ranges[i];
+      }
+      ranges.resize(m);
       QTile qt{};
       qt.q_fwd = (int32_t)(v.q_off + (a - v.qb));
       qt.q_row = (int32_t)(v.base + a);
       qt.n_tok = b - a;
       qt.kt_begin = (int32_t)p->ktiles.size();
-      size_t i = 0;
-      while (i < ranges.size()) {
-        int32_t s = ranges[i].first, e = ranges[i].second;
-        size_t j = i + 1;
-        while (j < ranges.size() && ranges[j].first <= e) {
-          e = std::max(e, ranges[j].second);
-          ++j;
+      // The ranges' keys in order, cut into 64-key tiles that run on across
+      // range ends (at most kMaxSegs ranges per tile), so that only the last
+      // tile of the tile's key list is short.
+      size_t r = 0;
+      int32_t x = m ? ranges[0].first : 0;
+      while (r < m) {
+        Seg sg[kMaxSegs];
+        int nseg = 0, n = 0;
+        bool full = true;
+        while (r < m && n < kKeyTile && nseg < kMaxSegs) {
+          const int32_t y = std::min(ranges[r].second, x + (kKeyTile - n));
+          sg[nseg].slot0 = n;
+          sg[nseg].row0 = (int32_t)(v.base + x);
+          ++nseg;
+          full = full && chunk_full(v, x, y, a, touched);
+          n += y - x;
+          x = y;
+          if (x == ranges[r].second && ++r < m) x = ranges[r].first;
         }
-        for (int32_t k0 = s; k0 < e; k0 += kKeyTile) {
-          const int32_t k1 = std::min(k0 + kKeyTile, e);
-          const bool full = (k1 - k0 == kKeyTile) && chunk_full(v, k0, k1, a, touched);
-          KTile kt{};
-          kt.k0 = (int32_t)(v.base + k0);
-          kt.meta = (k1 - k0) | (full ? 0 : kMaskedBit);
-          p->ktiles.push_back(kt);
-          p->kvis.push_back(Int2{0, INT32_MAX});
-          if (!full) ++p->n_masked_ktiles;
-        }
-        i = j;
+        emit_tile(sg, nseg, n, full && n == kKeyTile, Int2{0, INT32_MAX});
       }
       qt.kt_end = (int32_t)p->ktiles.size();
       if ((int64_t)p->ktiles.size() > (int64_t)INT32_MAX / 2)
@@ -543,14 +620,12 @@ static void build_image(ta_plan_s* p) {
   off = align256(off + p->qtiles.size() * sizeof(QTile));
   p->off_ktiles = off;
   off = align256(off + p->ktiles.size() * sizeof(KTile));
-  p->off_kvis = off;
-  off = align256(off + p->kvis.size() * sizeof(Int2));
+  p->off_mbits = off;
+  off = align256(off + p->mbits.size() * sizeof(uint32_t));
   p->off_segs = off;
   off = align256(off + p->segs.size() * sizeof(Seg));
   p->off_work = off;
   off = align256(off + p->work.size() * sizeof(int32_t));
-  p->off_anc = off;
-  off = align256(off + p->tok_anc.size() * sizeof(Int2));
   p->off_rowpos = off;
   off = align256(off + p->tok_rowpos.size() * sizeof(int32_t));
   p->off_posid = off;
@@ -567,10 +642,9 @@ static void build_image(ta_plan_s* p) {
   };
   put(p->off_qtiles, p->qtiles.data(), p->qtiles.size() * sizeof(QTile));
   put(p->off_ktiles, p->ktiles.data(), p->ktiles.size() * sizeof(KTile));
-  put(p->off_kvis, p->kvis.data(), p->kvis.size() * sizeof(Int2));
+  put(p->off_mbits, p->mbits.data(), p->mbits.size() * sizeof(uint32_t));
   put(p->off_segs, p->segs.data(), p->segs.size() * sizeof(Seg));
   put(p->off_work, p->work.data(), p->work.size() * sizeof(int32_t));
-  put(p->off_anc, p->tok_anc.data(), p->tok_anc.size() * sizeof(Int2));
   put(p->off_rowpos, p->tok_rowpos.data(), p->tok_rowpos.size() * sizeof(int32_t));
   put(p->off_posid, p->pos_id.data(), p->pos_id.size() * sizeof(int32_t));
 }
@@ -588,6 +662,7 @@ ta_status build_plan(const ta_tree_desc* desc, const ta_attn_cfg* cfg, ta_plan_s
   b.number_blocks();
   b.token_tables();
   if ((st = b.schedule()) != TA_OK) return st;
+  b.mask_bits();
   build_image(p);
   return TA_OK;
 }
@@ -638,6 +713,8 @@ ta_status tree_attn_plan_info(ta_plan_t p, ta_plan_info* out) {
   out->workspace_bytes = p->ws_bytes;
   out->num_segments = (int64_t)p->segs.size();
   out->batch_invariant = p->cfg.batch_invariant ? 1 : 0;
+  out->mask_words_per_tile = p->mask_words;
+  out->num_mask_words = (int64_t)p->mbits.size();
   return TA_OK;
 }
 
@@ -675,7 +752,7 @@ ta_status tree_attn_plan_schedule(ta_plan_t p, int32_t* q_tiles, int32_t* key_ti
     for (size_t i = 0; i < p->ktiles.size(); ++i) {
       const ta::KTile& t = p->ktiles[i];
       const int nseg = ((t.meta >> ta::kSegShift) & (ta::kMaxSegs - 1)) + 1;
-      int32_t* o = key_tiles + 7 * i;
+      int32_t* o = key_tiles + 8 * i;
       o[0] = nseg == 1 ? t.k0 : p->segs[t.k0].row0;
       o[1] = t.meta & 0xffff;
       o[2] = (t.meta & ta::kMaskedBit) ? 1 : 0;
@@ -683,6 +760,7 @@ ta_status tree_attn_plan_schedule(ta_plan_t p, int32_t* q_tiles, int32_t* key_ti
       o[4] = p->kvis[i].y;
       o[5] = nseg;
       o[6] = nseg == 1 ? -1 : t.k0 + 1;
+      o[7] = t.mblk;
     }
   if (segments)
     for (size_t i = 0; i < p->segs.size(); ++i) {
@@ -695,6 +773,13 @@ ta_status tree_attn_plan_schedule(ta_plan_t p, int32_t* q_tiles, int32_t* key_ti
       tok_anc[2 * i] = p->tok_anc[i].x;
       tok_anc[2 * i + 1] = p->tok_anc[i].y;
     }
+  return TA_OK;
+}
+
+ta_status tree_attn_plan_masks(ta_plan_t p, uint32_t* words) {
+  ta::clear_error();
+  if (!p || !words) return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (!p->mbits.empty()) memcpy(words, p->mbits.data(), p->mbits.size() * sizeof(uint32_t));
   return TA_OK;
 }
 

@@ -91,31 +91,73 @@ def test_plan_tables_bit_exact(lib, k):
     assert info["one_shot"] == int(one_shot)
 
 
+def _variant(group, head_dim):
+    """(waves, column groups) of the kernel variant, as the header states."""
+    if head_dim == 128:
+        return (8, 2) if group >= 4 else (4, 2 if group == 2 else 1)
+    return 4, min(group, 4)
+
+
+def decode_mask_bits(block, n_tok, group, head_dim):
+    """[n_tok, 64] visibility of (query token of the tile, key slot) from one
+    tile's block of bits in the documented lane layout; every lane holding the
+    same (token, slot) must agree, and every (token, slot) is held by a lane."""
+    waves, ncg = _variant(group, head_dim)
+    wpl = max(1, ncg // 2)
+    assert block.size == waves * 64 * wpl
+    v, lane, cg, ks, r = (a.ravel() for a in np.meshgrid(
+        np.arange(waves), np.arange(64), np.arange(ncg), np.arange(4), np.arange(4), indexing="ij"))
+    e = (4 * ks + r) * ncg + cg
+    bit = (block[(64 * v + lane) * wpl + e // 32] >> (e % 32).astype(np.uint32)) & 1
+    tok = np.minimum((16 * ncg * v + 16 * cg + lane % 16) // group, n_tok - 1)
+    cell = tok * 64 + 16 * ks + 4 * (lane // 16) + r
+    held = np.bincount(cell, minlength=n_tok * 64)
+    ones = np.bincount(cell, weights=bit, minlength=n_tok * 64)
+    assert (held > 0).all(), "every (token, slot) held by some lane"
+    assert ((ones == 0) | (ones == held)).all(), "lanes holding one (token, slot) agree"
+    return (ones > 0).reshape(n_tok, 64)
+
+
 def _expand_schedule(plan, idx, toks):
     """Apply the kernel's rule to the exported schedule: a tile's query tokens
-    see all keys of its unmasked key tiles, and the keys u of masked tiles that
-    count for t (lo <= P(t) < hi) with P(u) <= P(t) < E(u). Returns the
-    coverage count per (t, u)."""
+    see all keys of its unmasked key tiles, and on masked tiles the keys the
+    tile's visibility bits allow. The bits are first checked against the rule
+    they encode (the tile counts for t, lo <= P(t) < hi, and P(u) <= P(t) <
+    E(u); slots past the tile's keys never). Returns the coverage count per
+    (t, u)."""
     sch = P.tree_attn_plan_schedule(plan)
+    info = plan.info
+    masks = P.tree_attn_plan_masks(plan)
+    assert masks.shape[1] == info["mask_words_per_tile"]
+    assert masks.shape[0] == info["num_masked_key_tiles"] + 1 and not masks[0].any()
+    group = plan.cfg["num_q_heads"] // plan.cfg["num_kv_heads"]
     nq, nkv = idx.num_q_tokens, idx.num_kv_tokens
     cover = np.zeros((nq, nkv), np.int16)
     pre, end = sch["tok_anc"][:, 0], sch["tok_anc"][:, 1]
     seen_q = np.zeros(nq, np.int32)
+    blocks = []
     for qf, qr, n, kb, ke in sch["q_tiles"]:
         seen_q[qf:qf + n] += 1
         trows = np.arange(qr, qr + n)
         for i in range(kb, ke):
-            _, nk, masked, lo, hi, _, _ = sch["key_tiles"][i]
+            _, nk, masked, lo, hi, _, _, mblk = sch["key_tiles"][i]
             keys = key_tile_rows(sch, i)
             assert len(keys) == nk
             if masked:
                 pt = pre[trows]
-                vis = ((lo <= pt) & (pt < hi))[:, None] & (pre[keys][None, :] <= pt[:, None]) & \
-                      (pt[:, None] < end[keys][None, :])
+                rule = ((lo <= pt) & (pt < hi))[:, None] & (pre[keys][None, :] <= pt[:, None]) & \
+                    (pt[:, None] < end[keys][None, :])
+                bits = decode_mask_bits(masks[mblk], n, group, plan.cfg["head_dim"])
+                np.testing.assert_array_equal(bits[:, :nk], rule)
+                assert not bits[:, nk:].any(), "slots past the tile's keys are never visible"
+                vis = bits[:, :nk]
+                blocks.append(int(mblk))
             else:
+                assert mblk == 0
                 vis = np.ones((n, nk), bool)
             np.add.at(cover, (slice(qf, qf + n), keys), vis)
     assert np.all(seen_q == 1), "every query token in exactly one tile"
+    assert sorted(blocks) == list(range(1, len(blocks) + 1)), "one block per masked tile"
     return sch, cover
 
 
@@ -210,7 +252,7 @@ def test_tiles_by_prompt_position(lib, k):
             path = set(idx.block_anc[blk]) | {blk}
             js = []
             for i in range(kb, ke):
-                _, nk, masked, lo, hi, _, _ = sch["key_tiles"][i]
+                _, nk, masked, lo, hi, _, _, _ = sch["key_tiles"][i]
                 keys = key_tile_rows(sch, i)
                 counts = not masked or lo <= pre[tr] < hi
                 vis = np.ones(nk, bool) if not masked else \
@@ -290,7 +332,7 @@ def test_long_row_chunks_schedule_rows(lib):
                 tr = qr + (t - qf)
                 row = np.zeros(idx.num_kv_tokens, np.int16)
                 for i in range(kb, ke):
-                    _, nk, masked, lo, hi, _, _ = sch["key_tiles"][i]
+                    _, nk, masked, lo, hi, _, _, _ = sch["key_tiles"][i]
                     keys = key_tile_rows(sch, i)
                     if masked:
                         vis = (lo <= pre[tr] < hi) & (pre[keys] <= pre[tr]) & (pre[tr] < end[keys])
