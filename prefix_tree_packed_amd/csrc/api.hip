@@ -72,7 +72,8 @@ ta_status tree_attn_plan_upload(ta_plan_t p, void* d_workspace, size_t bytes, vo
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return ta::hip_fail(e, "querying the device");
-  const int per_cu = ta::attention_blocks_per_cu(p->cfg.head_dim, p->group, p->cfg.out_dtype == TA_F32);
+  const int per_cu = ta::attention_blocks_per_cu(p->cfg.head_dim, p->group, p->cfg.out_dtype == TA_F32,
+                                                 p->cfg.write_lse != 0);
   if (per_cu < 1) return ta::fail(TA_ERR_HIP, "attention kernel does not fit on a compute unit");
   long long n_wg = std::min<long long>((long long)cus * per_cu, ta::kMaxWorkgroups);
   if (p->max_workgroups > 0) n_wg = std::min<long long>(n_wg, p->max_workgroups);

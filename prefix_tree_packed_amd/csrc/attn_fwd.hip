@@ -155,7 +155,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int D, int G, int NCG, int WAVES, bool OUT_F32>
+template <int D, int G, int NCG, int WAVES, bool OUT_F32, bool LSE>
 __global__ void __launch_bounds__(WAVES * 64)
 tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                         const _Float16* __restrict__ V, void* __restrict__ Out,
@@ -607,20 +607,31 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     }
 
     // ---- the item's last tile: its scores are done, so Q is free ----------
-    const bool issued = issue_next();
+    // The next item's Q loads go out before this step's tile loads, so the
+    // end-of-tile wait (only the tile loads just issued may be outstanding)
+    // also covers them, and the output stores go out after that wait and the
+    // barrier, so neither waits for the stores to drain.
     const int o_q_fwd = tile.q_fwd, o_n_tok = tile.n_tok, o_kvh = c_kvh;
     const bool last = pos + 1 >= ie;
     if (!last) open_item(pos + 1);
+    const bool issued = issue_next();
     {
       h8 pb[2][NCG];
       probs(sa, pb);
       pv_product(s, pb);
     }
+    if (!last) end_of_tile(issued);
+    // Output of the finished item. A padded column (token >= n_tok) mirrors
+    // the tile's last token with head (column mod G), so it computed exactly
+    // what that real column computed and stores the same bytes to the same
+    // place: every path issues the same stores, which keeps the compiler's
+    // wait for the next item's Q loads from draining them. Each of a column's
+    // four lane groups holds its row sum and reference, so all four store the
+    // same LSE.
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
       const float lt = lacc[cg][0];
       const float inv = 1.0f / lt;
-      if ((wave * CPW + cg * 16 + l16) / G >= o_n_tok) continue;  // padded column
       const int o_tok = col_token(cg, o_n_tok), o_head = col_head(cg, o_kvh);
       const size_t obase = ((size_t)(o_q_fwd + o_tok) * hq + o_head) * D;
 #pragma unroll
@@ -634,12 +645,11 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
               h4{(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
         }
       }
-      if (Lse != nullptr && lg == 0)
+      if constexpr (LSE)
         Lse[(size_t)o_head * n_q_total + o_q_fwd + o_tok] =
             (mrun[cg] + __log2f(lt)) * 0.69314718055994530942f;
     }
     if (last) break;
-    end_of_tile(issued);
     ++pos;
   }
 }
@@ -662,9 +672,9 @@ cache_write_kernel(const _Float16* __restrict__ k_new, const _Float16* __restric
 
 // One entry per kernel variant: launch it (a != nullptr) or report how many of
 // its workgroups fit on a compute unit (a == nullptr, result in *per_cu).
-template <int D, int G, int NCG, int WAVES, bool F32>
+template <int D, int G, int NCG, int WAVES, bool F32, bool LSE>
 static hipError_t variant(const AttnArgs* a, hipStream_t st, int* per_cu) {
-  const auto kernel = tree_attn_fwd_kernel<D, G, NCG, WAVES, F32>;
+  const auto kernel = tree_attn_fwd_kernel<D, G, NCG, WAVES, F32, LSE>;
   if (!a) return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, kernel, WAVES * 64, 0);
   hipLaunchKernelGGL(kernel, dim3(a->n_wg), dim3(WAVES * 64), 0, st, (const _Float16*)a->q,
                      (const _Float16*)a->k, (const _Float16*)a->v, a->o, a->lse,
@@ -677,41 +687,45 @@ static hipError_t variant(const AttnArgs* a, hipStream_t st, int* per_cu) {
 }
 
 template <int D, int G>
-static hipError_t for_group(bool f32, const AttnArgs* a, hipStream_t st, int* per_cu) {
+static hipError_t for_group(bool f32, bool lse, const AttnArgs* a, hipStream_t st, int* per_cu) {
   constexpr int NCG = column_groups_for(G, D);
   constexpr int WAVES = waves_for(G, D);
-  return f32 ? variant<D, G, NCG, WAVES, true>(a, st, per_cu)
-             : variant<D, G, NCG, WAVES, false>(a, st, per_cu);
+  if (f32)
+    return lse ? variant<D, G, NCG, WAVES, true, true>(a, st, per_cu)
+               : variant<D, G, NCG, WAVES, true, false>(a, st, per_cu);
+  return lse ? variant<D, G, NCG, WAVES, false, true>(a, st, per_cu)
+             : variant<D, G, NCG, WAVES, false, false>(a, st, per_cu);
 }
 
 template <int D>
-static hipError_t for_dim(int group, bool f32, const AttnArgs* a, hipStream_t st, int* per_cu) {
+static hipError_t for_dim(int group, bool f32, bool lse, const AttnArgs* a, hipStream_t st,
+                          int* per_cu) {
   switch (group) {
-    case 1: return for_group<D, 1>(f32, a, st, per_cu);
-    case 2: return for_group<D, 2>(f32, a, st, per_cu);
-    case 4: return for_group<D, 4>(f32, a, st, per_cu);
-    case 8: return for_group<D, 8>(f32, a, st, per_cu);
+    case 1: return for_group<D, 1>(f32, lse, a, st, per_cu);
+    case 2: return for_group<D, 2>(f32, lse, a, st, per_cu);
+    case 4: return for_group<D, 4>(f32, lse, a, st, per_cu);
+    case 8: return for_group<D, 8>(f32, lse, a, st, per_cu);
     default: return hipErrorInvalidValue;
   }
 }
 
-static hipError_t for_variant(int head_dim, int group, bool f32, const AttnArgs* a, hipStream_t st,
-                              int* per_cu) {
+static hipError_t for_variant(int head_dim, int group, bool f32, bool lse, const AttnArgs* a,
+                              hipStream_t st, int* per_cu) {
   switch (head_dim) {
-    case 64: return for_dim<64>(group, f32, a, st, per_cu);
-    case 128: return for_dim<128>(group, f32, a, st, per_cu);
+    case 64: return for_dim<64>(group, f32, lse, a, st, per_cu);
+    case 128: return for_dim<128>(group, f32, lse, a, st, per_cu);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_tree_attention(const AttnArgs& a, hipStream_t st) {
   if (a.n_wg == 0) return hipSuccess;
-  return for_variant(a.head_dim, a.group, a.out_f32, &a, st, nullptr);
+  return for_variant(a.head_dim, a.group, a.out_f32, a.lse != nullptr, &a, st, nullptr);
 }
 
-int attention_blocks_per_cu(int head_dim, int group, bool out_f32) {
+int attention_blocks_per_cu(int head_dim, int group, bool out_f32, bool lse) {
   int per_cu = 0;
-  if (for_variant(head_dim, group, out_f32, nullptr, nullptr, &per_cu) != hipSuccess) return 0;
+  if (for_variant(head_dim, group, out_f32, lse, nullptr, nullptr, &per_cu) != hipSuccess) return 0;
   return per_cu;
 }
 

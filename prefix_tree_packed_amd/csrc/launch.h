@@ -23,9 +23,9 @@ struct AttnArgs {
 };
 
 hipError_t launch_tree_attention(const AttnArgs& a, hipStream_t st);
-// Workgroups of the attention kernel variant for (head_dim, group, out_f32)
+// Workgroups of the attention kernel variant for (head_dim, group, out_f32, lse)
 // that fit on one compute unit at once (0 if the variant does not exist).
-int attention_blocks_per_cu(int head_dim, int group, bool out_f32);
+int attention_blocks_per_cu(int head_dim, int group, bool out_f32, bool lse);
 hipError_t launch_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                               const void* tok_rowpos, int n_q, int hkv, int head_dim,
                               hipStream_t st);
