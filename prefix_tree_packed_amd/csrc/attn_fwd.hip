@@ -207,13 +207,13 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     vch[j] = 8 * ((lane % DCH) ^ v_swizzle<DCH>(row));
   }
 
-  auto issue = [&](int stage, int kvh, const KTile& t) {
+  // t: the tile's descriptor; sg: for a tile of several segments, segs[t.k0]
+  // .. segs[t.k0 + kMaxSegs] (header, then the segments), read ahead
+  auto issue = [&](int stage, int kvh, const KTile& t, const Seg (&sg)[kMaxSegs + 1]) {
     const int nk = t.meta & 0xffff;
     const int nseg = ((t.meta >> kSegShift) & (kMaxSegs - 1)) + 1;
     // slot 0's row: k0 itself for a one-segment tile, else from the header
-    // at segs[k0]
-    int k0 = t.k0;
-    if (nseg > 1) k0 = segs[t.k0].row0;
+    const int k0 = nseg > 1 ? sg[0].row0 : t.k0;
     const _Float16* kb = K + (size_t)kvh * D + (size_t)k0 * kv_stride;
     const _Float16* vb = V + (size_t)kvh * D + (size_t)k0 * kv_stride;
     // element offset of each loaded slot's row from slot 0's row: the slot
@@ -226,15 +226,18 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
 #pragma unroll
     for (int j = 0; j < IPW; ++j) roff[j] = lrow[j] < nk ? loff[j] : 0;
     if (nseg > 1) {
-      const Seg* sg = segs + t.k0 + 1;  // sg[0] starts at slot 0, row k0
       int rel[IPW];
 #pragma unroll
       for (int j = 0; j < IPW; ++j) rel[j] = lrow[j];
-      for (int k = 1; k < nseg; ++k) {
-        const Seg x = sg[k];
+      // segment k (k >= 1) is sg[1 + k]; segment 0 starts at slot 0, row k0
 #pragma unroll
-        for (int j = 0; j < IPW; ++j)
-          rel[j] = lrow[j] >= x.slot0 ? x.row0 - k0 + (lrow[j] - x.slot0) : rel[j];
+      for (int k = 1; k < kMaxSegs; ++k) {
+        if (k < nseg) {
+          const Seg x = sg[1 + k];
+#pragma unroll
+          for (int j = 0; j < IPW; ++j)
+            rel[j] = lrow[j] >= x.slot0 ? x.row0 - k0 + (lrow[j] - x.slot0) : rel[j];
+        }
       }
 #pragma unroll
       for (int j = 0; j < IPW; ++j) roff[j] = lrow[j] < nk ? rel[j] * (int)kv_stride : 0;
@@ -255,7 +258,12 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   // Load cursor: the workgroup's key tiles as one sequence over its items.
   // Every tile consumed issues the tile three places further on (which may
   // belong to a later item), so item boundaries do not drain the pipeline.
+  // The descriptor (and segment block) of the cursor's next tile is read one
+  // step ahead, at the end of the previous step, so the scalar loads are not
+  // waited for at the start of a step.
   int l_pos = ib, l_kt = 0, l_kte = 0, l_kvh = 0, l_stage = 0;
+  KTile l_desc{};
+  Seg l_sg[kMaxSegs + 1];
   auto l_open = [&]() {
     const int w = wg_items[l_pos];
     const int qt = w / hkv;
@@ -263,10 +271,19 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     l_kt = qtiles[qt].kt_begin;
     l_kte = qtiles[qt].kt_end;  // > kt_begin: a token always sees itself
   };
+  auto l_fetch = [&]() {
+    if (l_pos >= ie) return;
+    l_desc = ktiles[l_kt];
+    if ((l_desc.meta >> kSegShift) & (kMaxSegs - 1)) {  // several segments
+#pragma unroll
+      for (int k = 0; k <= kMaxSegs; ++k) l_sg[k] = segs[l_desc.k0 + k];
+    }
+  };
   l_open();
+  l_fetch();
   auto issue_next = [&]() {
     if (l_pos >= ie) return false;
-    issue(l_stage, l_kvh, ktiles[l_kt]);
+    issue(l_stage, l_kvh, l_desc, l_sg);
     l_stage = (l_stage + 1) & (kStages - 1);
     if (++l_kt >= l_kte && ++l_pos < ie) l_open();
     return true;
@@ -298,8 +315,11 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
 
   // first three tiles in flight together with the first item's Q fragments
   issue_next();
+  l_fetch();
   issue_next();
+  l_fetch();
   issue_next();
+  l_fetch();
   open_item(ib);
 
   f4 oacc[DT][NCG];
@@ -560,15 +580,19 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     __syncthreads();
     s = (s + 1) & (kStages - 1);
   };
-  auto step = [&](int kt, const f4 (&cur)[4][NCG], f4 (&nxt)[4][NCG]) {
+  // c_meta: meta of the compute cursor's next tile (kt + 1), read a step ahead
+  int c_meta = 0;
+  auto step = [&](int kt, int kte, const f4 (&cur)[4][NCG], f4 (&nxt)[4][NCG]) {
     const int s1 = (s + 1) & (kStages - 1);
     const bool issued = issue_next();
 
     float mx[NCG];
     fused(s1, s, cur, nxt, mx);
 
-    const KTile t1 = ktiles[kt + 1];
-    if (t1.meta & kMaskedBit) {
+    const bool masked = c_meta & kMaskedBit;
+    if (kt + 2 < kte) c_meta = ktiles[kt + 2].meta;
+    l_fetch();
+    if (masked) {
       apply_mask(s1, nxt);
       float m[NCG];
       tile_max_raw(nxt, m);
@@ -591,15 +615,16 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
       for (int dt = 0; dt < DT; ++dt) oacc[dt][cg] = f4{0.f, 0.f, 0.f, 0.f};
     }
     {
+      const int meta0 = ktiles[ktb].meta;
+      if (ktb + 1 < kte) c_meta = ktiles[ktb + 1].meta;
       s_product(s, sa);
-      const KTile t0 = ktiles[ktb];
-      if (t0.meta & kMaskedBit) apply_mask(s, sa);
+      if (meta0 & kMaskedBit) apply_mask(s, sa);
       float mx[NCG];
       tile_max_raw(sa, mx);
       move_reference(mx);
     }
     for (int kt = ktb; kt + 1 < kte; ++kt) {
-      step(kt, sa, sb);
+      step(kt, kte, sa, sb);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -615,6 +640,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     const bool last = pos + 1 >= ie;
     if (!last) open_item(pos + 1);
     const bool issued = issue_next();
+    l_fetch();
     {
       h8 pb[2][NCG];
       probs(sa, pb);

@@ -622,8 +622,10 @@ static void build_image(ta_plan_s* p) {
   off = align256(off + p->ktiles.size() * sizeof(KTile));
   p->off_mbits = off;
   off = align256(off + p->mbits.size() * sizeof(uint32_t));
+  // the kernel reads a multi-segment tile's header and kMaxSegs entries after
+  // it in one go: kMaxSegs zero entries of padding keep that in bounds
   p->off_segs = off;
-  off = align256(off + p->segs.size() * sizeof(Seg));
+  off = align256(off + (p->segs.size() + kMaxSegs) * sizeof(Seg));
   p->off_work = off;
   off = align256(off + p->work.size() * sizeof(int32_t));
   p->off_rowpos = off;
