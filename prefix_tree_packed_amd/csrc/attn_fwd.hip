@@ -575,8 +575,18 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   // The end of every consumed tile: the tile two places further on must have
   // landed (only the one just issued may still be in flight) and every wave
   // must be done with this tile's stage before it is refilled.
+  // The previous item's output stores (NST of them on every path, issued
+  // after its last barrier) sit between the tile loads of the first step of
+  // an item and the loads before them, so that step's wait lets them stay in
+  // flight too instead of draining them.
+  constexpr int NST = (OUT_F32 ? NCG * DT : NCG * DT / 2) + (LSE ? NCG : 0);
+  static_assert(LOADS + NST < 64, "vmcnt range");
+  bool stores_in_flight = false;
   auto end_of_tile = [&](bool issued) {
-    if (issued) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
+    if (!issued) wait_vmcnt<0>();
+    else if (stores_in_flight) wait_vmcnt<LOADS + NST>();
+    else wait_vmcnt<LOADS>();
+    stores_in_flight = false;
     __syncthreads();
     s = (s + 1) & (kStages - 1);
   };
@@ -619,9 +629,13 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
       if (ktb + 1 < kte) c_meta = ktiles[ktb + 1].meta;
       s_product(s, sa);
       if (meta0 & kMaskedBit) apply_mask(s, sa);
+      // the first reference is the tile's own column max (O and the row sums
+      // are still zero, so nothing is rescaled); a column that sees none of
+      // the tile's keys keeps a finite floor
       float mx[NCG];
       tile_max_raw(sa, mx);
-      move_reference(mx);
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) mrun[cg] = fmaxf(mx[cg] * scale_log2e, -1e30f);
     }
     for (int kt = ktb; kt + 1 < kte; ++kt) {
       step(kt, kte, sa, sb);
@@ -653,22 +667,34 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     // place: every path issues the same stores, which keeps the compiler's
     // wait for the next item's Q loads from draining them. Each of a column's
     // four lane groups holds its row sum and reference, so all four store the
-    // same LSE.
+    // same LSE. An f16 output goes out 16 bytes per lane: lane group g holds
+    // head-dim 16 dt + 4 g .. +3 of each dt, and one v_permlane16_swap per
+    // dword of a (dt, dt + 1) pair gives the even groups 8 consecutive values
+    // of dt and the odd groups those of dt + 1 (half as many stores).
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
       const float lt = lacc[cg][0];
       const float inv = 1.0f / lt;
       const int o_tok = col_token(cg, o_n_tok), o_head = col_head(cg, o_kvh);
       const size_t obase = ((size_t)(o_q_fwd + o_tok) * hq + o_head) * D;
+      if constexpr (OUT_F32) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const f4 val = oacc[dt][cg] * inv;
-        const int d0 = 16 * dt + 4 * lg;
-        if constexpr (OUT_F32) {
-          *(f4*)((float*)Out + obase + d0) = val;
-        } else {
-          *(h4*)((_Float16*)Out + obase + d0) =
-              h4{(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
+        for (int dt = 0; dt < DT; ++dt)
+          *(f4*)((float*)Out + obase + 16 * dt + 4 * lg) = oacc[dt][cg] * inv;
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < DT; dt += 2) {
+          const f4 ve = oacc[dt][cg] * inv, vo = oacc[dt + 1][cg] * inv;
+          const h2 e01 = h2{(_Float16)ve[0], (_Float16)ve[1]}, e23 = h2{(_Float16)ve[2], (_Float16)ve[3]};
+          const h2 o01 = h2{(_Float16)vo[0], (_Float16)vo[1]}, o23 = h2{(_Float16)vo[2], (_Float16)vo[3]};
+          // odd rows of the first operand trade places with even rows of the second
+          const auto w0 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, e01),
+                                                           __builtin_bit_cast(unsigned, o01), false, false);
+          const auto w1 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, e23),
+                                                           __builtin_bit_cast(unsigned, o23), false, false);
+          typedef unsigned u4 __attribute__((ext_vector_type(4)));
+          const int d0 = 16 * (dt + (lg & 1)) + 8 * (lg >> 1);
+          *(u4*)((_Float16*)Out + obase + d0) = u4{w0[0], w1[0], w0[1], w1[1]};
         }
       }
       if constexpr (LSE)
@@ -676,6 +702,9 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
             (mrun[cg] + __log2f(lt)) * 0.69314718055994530942f;
     }
     if (last) break;
+    // the stores above stay ahead of the next item's tile loads
+    asm volatile("" ::: "memory");
+    stores_in_flight = true;
     ++pos;
   }
 }
