@@ -195,7 +195,7 @@ ta_status tree_attn_plan_export(ta_plan_t plan, int32_t* pos_id, int32_t* tok_ro
  *           token, row-space index of its first token, tokens, first key tile,
  *           end key tile)
  *   key_tiles [num_key_tiles * 8]: per key tile (row-space key of slot 0,
- *           keys n, 1 if the kernel applies the per-key visibility test else 0,
+ *           keys n, 1 if the kernel applies the tile's visibility bits else 0,
  *           lo, hi, segment count, first segment, visibility block): the tile
  *           counts for query t only if lo <= P(t) < hi; with one segment slot
  *           s holds key k0 + s, otherwise segments[first .. first + count) map
@@ -210,8 +210,9 @@ ta_status tree_attn_plan_export(ta_plan_t plan, int32_t* pos_id, int32_t* tok_ro
  *           t iff P(u) <= P(t) < E(u)
  *   segments [num_segments * 2]: (first slot, row-space key of that slot); a
  *           segment runs to the next one's first slot (the last to n). The
- *           entry before each tile's first segment is a header the kernel
- *           uses (where the tile's per-key entries start, slot 0's key)
+ *           entry before each tile's first segment is a header (where the
+ *           tile's own copies of its slots' (P, E) entries start in the host
+ *           table, slot 0's key)
  */
 ta_status tree_attn_plan_schedule(ta_plan_t plan, int32_t* q_tiles, int32_t* key_tiles,
                                   int32_t* work, int32_t* tok_anc, int32_t* segments);

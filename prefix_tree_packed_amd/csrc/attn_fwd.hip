@@ -73,8 +73,8 @@ __device__ __forceinline__ float column_max(float x) {
 // ---------------------------------------------------------------------------
 // Data movement. The K and V tiles travel from global memory straight into LDS
 // (global_load_lds_dwordx4), rows XOR-swizzled at 16-byte granularity, and the
-// V^T operand of the P.V product is read with ds_read_b64_tr_b16. Three LDS
-// stages let each tile's loads overlap two tiles of math.
+// V^T operand of the P.V product is read with ds_read_b64_tr_b16. Four LDS
+// stages (kStages below) let each tile's loads overlap two tiles of math.
 //
 // The two tiles use different swizzles because they are read differently. A K
 // read (ds_read_b128) has 16 lanes fetch one logical chunk of 16 consecutive
@@ -291,7 +291,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
 
   // ---- the item being computed: its query tile and the lane's columns ------
   // Column c of a tile is (token c / G, head kvh * G + c % G); padded columns
-  // (token >= n_tok) mirror the tile's last token and are not stored. Columns
+  // (token >= n_tok) mirror the tile's last token (and store what it stores). Columns
   // are recomputed from the tile where needed rather than kept in registers.
   int c_kvh = 0;
   QTile tile;

@@ -25,7 +25,7 @@ struct QTile {
 // (some key is not visible to every query of the tile, or the tile is short),
 // and nseg - 1 in bits 17-19. With one segment, slot s holds row-space key
 // k0 + s. With several, k0 is an index h into the segment table: segs[h] =
-// {first (P, E) entry of the tile's slots, row of slot 0} and segs[h + 1 ..
+// {first (P, E) entry of the tile's slots (host tables only), row of slot 0} and segs[h + 1 ..
 // h + nseg] are the segments (Seg below). `mblk` is the tile's block of
 // visibility bits (see mask_words_per_lane); unflagged tiles point at block 0, which
 // is all zero and never read.
