@@ -336,45 +336,75 @@ void Builder::mask_bits() {
   const int wpl = mask_words_per_lane(G, D);
   const int mw = mask_words_per_tile(G, D);
   p->mask_words = mw;
-  p->mbits.assign(mw, 0u);
-  std::vector<uint64_t> tokvis;  // per query token of the tile: bit s = slot s visible
+  p->mbits.assign((size_t)(p->n_masked_ktiles + 1) * mw, 0u);
+  // spread[m]: bit r of the nibble m moved to bit r * ncg (element e of slot
+  // 16 ks + 4 g + r is bit (4 ks + r) * ncg + cg of the lane's bits)
+  uint64_t spread[16];
+  for (int m = 0; m < 16; ++m) {
+    spread[m] = 0;
+    for (int r = 0; r < 4; ++r)
+      if ((m >> r) & 1) spread[m] |= uint64_t(1) << (r * ncg);
+  }
+  struct Run {
+    int32_t slot0, len, p0, end;  // slots [slot0, slot0 + len): positions p0 .., subtree end
+  };
+  std::vector<Run> runs;
+  std::vector<uint64_t> pat;  // per (token, lane group): the lane's bits for column group 0
+  std::vector<int32_t> ctok(16 * ncg * waves);  // query token of each column of the tile
+  int32_t blk = 0;
   for (const QTile& q : p->qtiles) {
+    bool have_ctok = false;
     for (int32_t k = q.kt_begin; k < q.kt_end; ++k) {
       KTile& t = p->ktiles[k];
       if (!(t.meta & kMaskedBit)) {
         t.mblk = 0;
         continue;
       }
+      t.mblk = ++blk;
+      if (!have_ctok) {
+        for (int c = 0; c < (int)ctok.size(); ++c) ctok[c] = std::min(c / G, q.n_tok - 1);
+        have_ctok = true;
+      }
       const int32_t n = t.meta & 0xffff;
       const int nseg = ((t.meta >> kSegShift) & (kMaxSegs - 1)) + 1;
       const Int2* ue = p->tok_anc.data() + (nseg == 1 ? t.k0 : p->segs[t.k0].slot0);
+      // the tile's slots in runs of one block each: consecutive positions,
+      // one subtree end; key u is visible to query t iff P(u) <= P(t) < E(u),
+      // so a run shows a token its first min(P(t) - p0 + 1, len) slots
+      runs.clear();
+      for (int32_t s = 0; s < n; ++s) {
+        if (!runs.empty() && ue[s].y == runs.back().end &&
+            ue[s].x == runs.back().p0 + runs.back().len && s == runs.back().slot0 + runs.back().len)
+          ++runs.back().len;
+        else
+          runs.push_back(Run{s, 1, ue[s].x, ue[s].y});
+      }
       const Int2 vis = p->kvis[k];
-      tokvis.assign(q.n_tok, 0);
+      pat.assign((size_t)q.n_tok * 4, 0);
       for (int32_t i = 0; i < q.n_tok; ++i) {
         const int32_t pt = p->tok_anc[q.q_row + i].x;
         if (pt < vis.x || pt >= vis.y) continue;
-        uint64_t w = 0;
-        for (int32_t s = 0; s < n; ++s)
-          if (ue[s].x <= pt && pt < ue[s].y) w |= uint64_t(1) << s;
-        tokvis[i] = w;
+        uint64_t tv = 0;
+        for (const Run& r : runs) {
+          if (pt >= r.end || pt < r.p0) continue;
+          const int32_t c = std::min(pt - r.p0 + 1, r.len);
+          tv |= (c >= 64 ? ~uint64_t(0) : ((uint64_t(1) << c) - 1)) << r.slot0;
+        }
+        for (int g = 0; g < 4; ++g) {
+          uint64_t w = 0;
+          for (int ks = 0; ks < 4; ++ks) w |= spread[(tv >> (16 * ks + 4 * g)) & 15] << (4 * ncg * ks);
+          pat[(size_t)i * 4 + g] = w;
+        }
       }
-      t.mblk = (int32_t)(p->mbits.size() / mw);
-      const size_t base = p->mbits.size();
-      p->mbits.resize(base + mw, 0u);
-      uint32_t* blk = p->mbits.data() + base;
+      uint32_t* out = p->mbits.data() + (size_t)blk * mw;
       for (int w = 0; w < waves; ++w)
         for (int lane = 0; lane < 64; ++lane) {
-          uint32_t* lw = blk + ((size_t)w * 64 + lane) * wpl;
-          for (int cg = 0; cg < ncg; ++cg) {
-            const int col = 16 * ncg * w + 16 * cg + lane % 16;
-            const uint64_t tv = tokvis[std::min(col / G, q.n_tok - 1)];
-            for (int ks = 0; ks < 4; ++ks)
-              for (int r = 0; r < 4; ++r) {
-                const int slot = 16 * ks + 4 * (lane / 16) + r;
-                const int e = (4 * ks + r) * ncg + cg;
-                if ((tv >> slot) & 1) lw[e / 32] |= 1u << (e % 32);
-              }
-          }
+          const int32_t* ct = ctok.data() + 16 * ncg * w + (lane & 15);
+          const uint64_t* pg = pat.data() + (lane >> 4);
+          uint64_t bits = 0;
+          for (int cg = 0; cg < ncg; ++cg) bits |= pg[(size_t)ct[16 * cg] * 4] << cg;
+          uint32_t* lw = out + ((size_t)w * 64 + lane) * wpl;
+          for (int j = 0; j < wpl; ++j) lw[j] = (uint32_t)(bits >> (32 * j));
         }
     }
   }
