@@ -220,7 +220,8 @@ namespace ta {
 constexpr int kReadoutMaxModel = 16384;
 
 // K splits of the down projection: a function of the weight shape only (so a
-// row's sums never depend on the batch), enough to give about 512 workgroups.
+// row's sums never depend on the batch): about 512 (64-row column block, split)
+// pairs, i.e. about 256 eight-wave workgroups.
 static int readout_splits(int d_model, int d_ff) {
   const int col_blocks = d_model / 64;
   int ks = 8;

@@ -22,10 +22,10 @@
 //
 // The projections are skinny products (a few dozen rows against 14k-28k
 // weight rows), bound by streaming the weights once from HBM. A workgroup owns
-// 64 weight rows, 16 per wave, and runs v_mfma_f32_16x16x32_f16 with the
+// 128 weight rows, 16 per wave, and runs v_mfma_f32_16x16x32_f16 with the
 // weight rows as the A operand (8 consecutive K values per lane, streamed from
 // global memory through a register ring several steps deep) and the
-// activation rows as the B operand (staged in LDS, shared by the four waves).
+// activation rows as the B operand (staged in LDS, shared by the eight waves).
 // Each output is one wave's MFMA chain over its K range in K order, and the
 // down product's K splits are fixed by the weight shape and summed in split
 // order, so nothing in a row's arithmetic depends on how many rows are in the
@@ -121,22 +121,23 @@ readout_norm_kernel(const _Float16* __restrict__ hidden, long long n_tokens,
   }
 }
 
-// One workgroup: 64 weight rows, 16 per wave (one MFMA A fragment), against
+// One workgroup: WAVES * 16 weight rows, 16 per wave (one MFMA A fragment), against
 // one pass of MF*16 activation rows (the B fragments), over the K range
 // [split * k_len, (split + 1) * k_len). Every output is one wave's MFMA chain
 // over that range in K order.
 //   GATE_UP: w0 is the interleaved gate/up matrix (16-row blocks: gate rows
 //            8i .. 8i+7, then the up rows of the same columns); wave w streams
-//            block 4*blockIdx + w, so its fragment rows 0-7 are gate rows
+//            block WAVES*unit + w, so its fragment rows 0-7 are gate rows
 //            j0+8w .. j0+8w+7 and rows 8-15 the up rows of the same columns, and
 //            a lane and the lane 32 above it hold gate and up of one output;
-//            act[m][j0 .. j0+31] (f16). A workgroup reads 64 consecutive rows:
-//            one stream, whatever the weight allocation (two matrices read in
-//            lockstep alias on HBM channels when their distance is unlucky).
+//            act[m][j0 .. j0+8*WAVES-1] (f16). A workgroup reads WAVES*16
+//            consecutive rows: one stream, whatever the weight allocation (two
+//            matrices read in lockstep alias on HBM channels when their
+//            distance is unlucky).
 //   !GATE_UP: wave w's rows are w0 rows j0+16w .. j0+16w+15 (the down
-//            projection); output f32 partial[split][m][j0 .. j0+63].
+//            projection); output f32 partial[split][m][j0 .. j0+16*WAVES-1].
 // The activation rows of a 256-deep K slice are staged in LDS (two buffers,
-// shared by the 4 waves); each wave streams its weight fragments through a
+// shared by the waves); each wave streams its weight fragments through a
 // register ring kRing steps deep.
 constexpr int kSlice = 256;               // K per LDS stage
 constexpr int kSteps = kSlice / kStepK;   // pipeline steps per stage
@@ -372,11 +373,11 @@ letter_logits_kernel(const _Float16* __restrict__ h, int dm, const _Float16* __r
   }
 }
 
-// Up to 64 activation rows: one pass, 4 waves (64 weight rows) per workgroup.
-// More: passes of 128 rows with 8 waves (128 weight rows) per workgroup, so
-// the weights stream once per 128 rows and the staged activations per thread
-// stay the same (135 KB of LDS: one workgroup per CU). Each pass is a
-// workgroup of its own.
+// Every pass runs 8 waves (128 weight rows) per workgroup, so each staged
+// activation row serves twice the weight bytes of a 4-wave workgroup (2-3%
+// faster at 14 and 64 rows than 4 waves). Up to 64 activation rows: one pass.
+// More: passes of 128 rows, so the weights stream once per 128 rows (135 KB of
+// LDS: one workgroup per CU). Each pass is a workgroup of its own.
 template <int MF, bool GU, int WAVES>
 hipError_t launch_mlp(const _Float16* x, int ldx, const _Float16* w0, int ldw,
                       int n_rows, int k_len, int splits, int out_cols, _Float16* act,
@@ -396,13 +397,13 @@ hipError_t launch_mlp_rows(const _Float16* x, int ldx, const _Float16* w0, int l
                            int k_len, int splits, int out_cols, _Float16* act, int ld_act,
                            float* partial, int ld_part, hipStream_t st) {
   if (n_rows <= 16)
-    return launch_mlp<1, GU, 4>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
+    return launch_mlp<1, GU, 8>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
                                 partial, ld_part, st);
   if (n_rows <= 32)
-    return launch_mlp<2, GU, 4>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
+    return launch_mlp<2, GU, 8>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
                                 partial, ld_part, st);
   if (n_rows <= 64)
-    return launch_mlp<4, GU, 4>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
+    return launch_mlp<4, GU, 8>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
                                 partial, ld_part, st);
   return launch_mlp<8, GU, 8>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
                               partial, ld_part, st);
