@@ -316,6 +316,8 @@ readout_finish_kernel(const _Float16* __restrict__ hidden, long long n_tokens,
   *(h8*)(h_out + (size_t)m * dm + (size_t)c * 8) = q;
 }
 
+constexpr int kLetterBatch = 8;  // head-row chunks in flight per lane
+
 // One workgroup per readout row: final RMS norm (f16 result kept in LDS), then
 // wave w computes letters w, w+4, ...: a lane-sequential f32 dot over its
 // 8-element chunks, then the fixed butterfly.
@@ -362,11 +364,22 @@ letter_logits_kernel(const _Float16* __restrict__ h, int dm, const _Float16* __r
     }
     const _Float16* row = lm_head + (size_t)id * dm;
     float acc = 0.f;
-    for (int c = lane; c < nc; c += 64) {
-      const h8 a = *(const h8*)(row + (size_t)c * 8);
-      const h8 b = y[c];
+    // The head row's chunks are loaded kLetterBatch at a time before any is
+    // used, so their memory latencies overlap; the sum still runs over the
+    // lane's chunks in increasing order.
+    for (int c0 = lane; c0 < nc; c0 += 64 * kLetterBatch) {
+      h8 a[kLetterBatch];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
+      for (int u = 0; u < kLetterBatch; ++u)
+        if (c0 + 64 * u < nc) a[u] = *(const h8*)(row + (size_t)(c0 + 64 * u) * 8);
+#pragma unroll
+      for (int u = 0; u < kLetterBatch; ++u) {
+        if (c0 + 64 * u < nc) {
+          const h8 b = y[c0 + 64 * u];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc = fmaf((float)a[u][e], (float)b[e], acc);
+        }
+      }
     }
     acc = wave_sum(acc);
     if (lane == 0) out[j] = acc;
