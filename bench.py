@@ -1,6 +1,6 @@
 """Throughput of prefix-tree-packed tree attention + the decision epilogue on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--seed 0]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config all|0-4[,..]] [--seed 0]
 
 One step = one pass of the device hot path over one batch: for every forward
 of the workload, the chunk's K/V cache write and the tree-attention launch
@@ -10,6 +10,10 @@ epilogue for the batch. The plan (host validation, token tables, block-sparse
 schedule, upload) is built once per batch before the timed region: it is
 shared by every layer of a model, and its host time is reported as
 plan_build_ms. Inputs are resident in HBM before timing starts.
+
+By default the four 8192-token workloads (configs 1-4) are timed one after
+the other; the first (the Llama-8B-shaped forward) is the headline and the
+others are reported under `configs` with the same per-launch figures.
 
 Prints one JSON line. `value` is useful tree-attention TFLOP/s over the whole
 step (useful FLOPs = 4 * head_dim * q_heads * sum over query tokens of the
@@ -78,11 +82,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", default="all",
+                    help="workload index 0-4, a comma list, or 'all' (the 8192-token workloads "
+                         "1,2,3,4; the first listed of them is the headline)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--out-dtype", default="f16", choices=["f16", "f32"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target wall time of the CPU-oracle sample")
+                    help="target wall time of the headline workload's CPU-oracle sample "
+                         "(the other workloads get half of it each)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--batch-invariant", action="store_true",
                     help="key tiles by position in each query's own prompt (bitwise-identical "
@@ -100,22 +107,24 @@ def parse():
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                          "(multi-GPU sharding is described in DESIGN.md, not implemented)"}))
-        sys.exit(2)
+def config_list(arg: str):
+    if arg == "all":
+        return [1, 2, 3, 4]
+    out = [int(x) for x in arg.split(",") if x.strip()]
+    if not out or any(c < 0 or c > 4 for c in out):
+        raise SystemExit(f"--config: expected indices 0-4 or 'all', got {arg!r}")
+    return out
 
+
+def bench_config(cfg: int, args, dev, stream):
+    """Times one workload: for each step, every forward's cache write and
+    attention launch, then the batch's decisions. Returns the measurements and
+    what the rest of the report needs (workload, plans, plan infos)."""
     import torch
     import prefix_tree_packed_amd as P
     from workloads import make_config
 
-    assert torch.cuda.is_available(), "bench needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    wl = make_config(args.config, args.seed)
-    stream = torch.cuda.current_stream()
+    wl = make_config(cfg, args.seed)
 
     def T(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -138,10 +147,8 @@ def main():
         if cache is None or not shared:
             kc, vc = f.cache_before()
             cache = (T(kc), T(vc))
-            cache0 = (cache[0].clone(), cache[1].clone())
-        fw.append(dict(q=T(f.q), kn=T(kn), vn=T(vn), kc=cache[0], vc=cache[1], kc0=cache0[0],
-                       vc0=cache0[1], o=torch.empty((info["num_q_tokens"], wl.hq, wl.d), dtype=odt,
-                                                   device=dev)))
+        fw.append(dict(q=T(f.q), kn=T(kn), vn=T(vn), kc=cache[0], vc=cache[1],
+                       o=torch.empty((info["num_q_tokens"], wl.hq, wl.d), dtype=odt, device=dev)))
     d = wl.decisions
     logits, row1, row2 = T(d.logits), T(d.row1), T(d.row2)
     nl, temps = T(d.n_letters), T(d.T)
@@ -216,27 +223,45 @@ def main():
     write_gbps = sum(write_bytes) / (write_ms.sum() * 1e-3) / 1e9
     # K and V of every row-space key a forward's queries may see, read once
     kv_bytes = [2 * inf["num_kv_tokens"] * wl.hkv * wl.d * 2 for inf in infos]
+    alg_bytes = [algorithmic_bytes(p, wl, args.out_dtype) for p in plans]
 
-    alg_bytes_k = algorithmic_bytes(plans[k], wl, args.out_dtype)
-    out = {
-        "metric": "useful tree-attention TFLOP/s (packed tokens/s and % of f16 MFMA peak alongside)",
-        "value": round(value, 3),
+    # correctness guard on the timed outputs (cheap): finite everywhere
+    for x in fw:
+        assert torch.isfinite(x["o"].float()).all().item(), "non-finite attention output"
+
+    traffic = [None] * n_fw
+    if args.seed == 0 and args.out_dtype == "f16" and not args.batch_invariant and not args.rope:
+        traffic = [measured_traffic(cfg, j) for j in range(n_fw)]
+    roofline = {
+        "bound": "mfma",
+        "kernel": "tree_attn_fwd_kernel",
+        "achieved": round(achieved, 3),
+        "peak": PEAK_F16_TFLOPS,
         "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic",
-        "packed_tokens_per_s": round(q_tokens / (ms_per_step * 1e-3), 1),
-        "pct_mfma_peak": round(100 * value / PEAK_F16_TFLOPS, 2),
-        "attention_only_tflops": round(attn_total_tflops, 3),
+        "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+        "traffic": None,
+        "per_launch": {"useful_flop": useful_flops[k], "avg_ms": round(float(attn_ms_mean[k]), 5),
+                       "forward_index": k,
+                       "algorithmic_bytes": alg_bytes[k],
+                       "algorithmic_gbps": round(alg_bytes[k] / (attn_ms_mean[k] * 1e-3) / 1e9, 1)},
+    }
+    if traffic[k] is not None:
+        roofline["traffic"] = traffic[k]["fetch_bytes"] + traffic[k]["write_bytes"]
+        roofline["traffic_detail"] = dict(traffic[k], source=os.path.relpath(TRAFFIC_FILE, ROOT))
+    res = {
+        "value": value,
+        "ms_per_step": ms_per_step,
+        "packed_tokens_per_s": q_tokens / (ms_per_step * 1e-3),
+        "attention_only_tflops": attn_total_tflops,
         "attention_ms_per_forward": [round(float(x), 5) for x in attn_ms_mean],
         "attention_ms_p10_p50_p90": [[round(float(np.percentile(attn_ms[:, j], q)), 5) for q in (10, 50, 90)]
                                      for j in range(n_fw)],
+        "attention_tflops_per_forward": [round(fl / (t * 1e-3) / 1e12, 1)
+                                         for fl, t in zip(useful_flops, attn_ms_mean)],
+        "algorithmic_gbps_per_forward": [round(b / (t * 1e-3) / 1e9, 1) for b, t in zip(alg_bytes, attn_ms_mean)],
+        "traffic_bytes_per_forward": [None if t is None else t["fetch_bytes"] + t["write_bytes"]
+                                      for t in traffic],
+        "algorithmic_bytes_per_forward": alg_bytes,
         "kv_stream_gbps_per_forward": [round(kv / (t * 1e-3) / 1e9, 1) for kv, t in zip(kv_bytes, attn_ms_mean)],
         "cache_write": {"kernel": "rope_cache_write_kernel" if args.rope else "cache_write_kernel",
                         "bound": "hbm", "us_per_forward": [round(float(x) * 1e3, 2) for x in write_ms],
@@ -244,7 +269,7 @@ def main():
                         "peak_gbps": 8000.0, "frac": round(write_gbps / 8000.0, 4)},
         "plan_build_ms": round(plan_build_ms, 3),
         "config": {
-            "workload": f"config[{args.config}] {wl.name}",
+            "workload": f"config[{cfg}] {wl.name}",
             "seed": args.seed,
             "forwards": n_fw,
             "q_tokens_per_forward": [i["num_q_tokens"] for i in infos],
@@ -256,37 +281,90 @@ def main():
             "key_tiling": "by prompt position" if args.batch_invariant else "union",
             "rope": args.rope,
         },
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "tree_attn_fwd_kernel",
-            "achieved": round(achieved, 3),
-            "peak": PEAK_F16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_F16_TFLOPS, 4),
-            "traffic": None,
-            "per_launch": {"useful_flop": useful_flops[k], "avg_ms": round(float(attn_ms_mean[k]), 5),
-                           "forward_index": k,
-                           "algorithmic_bytes": alg_bytes_k,
-                           "algorithmic_gbps": round(alg_bytes_k / (attn_ms_mean[k] * 1e-3) / 1e9, 1)},
-        },
+        "roofline": roofline,
     }
+    return res, wl, plans, infos
 
-    tr = (measured_traffic(args.config, k)
-          if args.seed == 0 and args.out_dtype == "f16" and not args.batch_invariant and not args.rope
-          else None)
-    if tr is not None:
-        out["roofline"]["traffic"] = tr["fetch_bytes"] + tr["write_bytes"]
-        out["roofline"]["traffic_detail"] = dict(tr, source=os.path.relpath(TRAFFIC_FILE, ROOT))
 
-    # correctness guard on the timed outputs (cheap): finite everywhere
-    for x in fw:
-        assert torch.isfinite(x["o"].float()).all().item(), "non-finite attention output"
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                          "(multi-GPU sharding is described in DESIGN.md, not implemented)"}))
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    cfgs = config_list(args.config)
+
+    results = {}
+    for c in cfgs:
+        print(f"[bench] config {c}", file=sys.stderr, flush=True)
+        results[c] = bench_config(c, args, dev, stream)
+        if len(cfgs) > 1:     # free the workload's device buffers before the next
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+    head = cfgs[0]
+    res, wl, plans, infos = results[head]
+    out = {
+        "metric": "useful tree-attention TFLOP/s (packed tokens/s and % of f16 MFMA peak alongside)",
+        "value": round(res["value"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "packed_tokens_per_s": round(res["packed_tokens_per_s"], 1),
+        "pct_mfma_peak": round(100 * res["value"] / PEAK_F16_TFLOPS, 2),
+        "attention_only_tflops": round(res["attention_only_tflops"], 3),
+    }
+    for key in ("attention_ms_per_forward", "attention_ms_p10_p50_p90", "attention_tflops_per_forward",
+                "kv_stream_gbps_per_forward", "cache_write", "plan_build_ms", "config", "roofline"):
+        out[key] = res[key]
+
+    if len(cfgs) > 1:
+        # every timed workload: attention alone (HIP events around each launch)
+        # and the whole step, useful TFLOP/s and fraction of the f16 MFMA peak
+        per = {}
+        for c in cfgs:
+            r = results[c][0]
+            a = r["attention_only_tflops"]
+            per[f"config[{c}]"] = {
+                "workload": r["config"]["workload"],
+                "attention_tflops": round(a, 1),
+                "attention_frac": round(a / PEAK_F16_TFLOPS, 4),
+                "step_tflops": round(r["value"], 1),
+                "ms_per_step": round(r["ms_per_step"], 5),
+                "packed_tokens_per_s": round(r["packed_tokens_per_s"], 1),
+                "useful_gflop_per_step": r["config"]["useful_gflop_per_step"],
+                "attention_ms_per_forward": r["attention_ms_per_forward"],
+                "attention_tflops_per_forward": r["attention_tflops_per_forward"],
+                "algorithmic_bytes_per_forward": r["algorithmic_bytes_per_forward"],
+                "algorithmic_gbps_per_forward": r["algorithmic_gbps_per_forward"],
+                "traffic_bytes_per_forward": r["traffic_bytes_per_forward"],
+                "cache_write_gbps": r["cache_write"]["achieved_gbps"],
+                "roofline_frac_heaviest_launch": r["roofline"]["frac"],
+            }
+        out["configs"] = per
+        flops = sum(results[c][0]["config"]["useful_gflop_per_step"] for c in cfgs)
+        attn_s = sum(sum(results[c][0]["attention_ms_per_forward"]) for c in cfgs) * 1e-3
+        out["configs_aggregate"] = {"attention_tflops": round(flops / attn_s / 1e3, 1),
+                                    "attention_frac": round(flops / attn_s / 1e3 / PEAK_F16_TFLOPS, 4)}
 
     if not args.no_readout:
         out["readout"] = bench_readout(args, wl, plans, dev, stream)
     if not args.no_mfma_probe:
         probe = mfma_attainable(dev, stream)
-        probe["attention_pct_of_attainable"] = round(100 * achieved / probe["tflops"], 2)
+        probe["attention_pct_of_attainable"] = round(100 * res["roofline"]["achieved"] / probe["tflops"], 2)
         out["mfma_attainable"] = probe
 
     if args.copy_calibration:
@@ -299,6 +377,10 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, infos, args.cpu_seconds)
+        if len(cfgs) > 1:
+            for c in cfgs[1:]:
+                _, wlc, _, infc = results[c]
+                out["configs"][f"config[{c}]"]["cpu_baseline"] = cpu_baseline(wlc, infc, args.cpu_seconds / 2)
     print(json.dumps(out), flush=True)
 
 

@@ -263,7 +263,12 @@ ta_status tree_attn_plan_destroy(ta_plan_t plan);
 
 /*
  * One-shot tree attention: every row is computed whole (info.one_shot == 1),
- * so query index == row-space index.
+ * so query index == row-space index. What it computes is section 03 "Packing",
+ * "Attention over tree blocks" (a token sees the earlier tokens of its own
+ * block and every token of its ancestor blocks; siblings are masked, so each
+ * token gets what its full prompt run alone gives) over the compact f16 token
+ * list of section 01 stage "GPU forward pass" (no padding, attention
+ * accumulated in f32).
  *   q   [T_q, Hq, D] f16        k, v [T_q, Hkv, D] f16
  *   o   [T_q, Hq, D] out_dtype  lse  [Hq, T_q] f32 natural-log sum-exp, or NULL
  * O[t,h] = sum_u P[t,u] V[u,kv] with P the softmax over the keys u that t may
@@ -276,8 +281,13 @@ ta_status tree_attn_forward(ta_plan_t plan, const void* q, const void* k, const 
                             void* o, float* lse, void* hip_stream);
 
 /*
- * Chunked tree attention against a row-space K/V cache (long rows computed as
- * forwards of at most 8,192 tokens, and a template cached at start-up).
+ * Chunked tree attention against a row-space K/V cache: the same attention as
+ * tree_attn_forward (section 03 "Attention over tree blocks") for forwards
+ * that compute part of a row, because a row holds up to 32,768 tokens but one
+ * forward at most 8,192 (section 01 "Batch and prefix tree"), and because the
+ * template is computed once at start-up and only its K/V are reused (section
+ * 03 "Packing"). Keys of a row's tokens before row_q_begin come from the
+ * cache; this forward's own keys are written there first.
  *   q              [T_q, Hq, D] f16, this forward's tokens in forward order
  *   k_new, v_new   [T_q, Hkv, D] f16, their keys and values
  *   k_cache, v_cache [cache_tokens, Hkv, D] f16 in row space; on entry rows'
@@ -437,10 +447,15 @@ ta_status letter_logits(const void* h, int32_t n_readout, int32_t d_model, const
  *   T         [n_dec] f32 device        temperature of decision i
  *   p_avg, p_cal [n_dec, ld] f32 device outputs, unrounded; columns >= n_letters[i] are 0
  * Host-checked: pointers non-null, ld >= 2, n_rows >= 1, n_dec >= 0 (0: nothing is
- * launched). Per-decision values live on the device and are checked by the kernel:
- * a decision with a row outside [0, n_rows), n_letters outside [2, min(ld, 255)]
+ * launched); these return an error with nothing launched. Per-decision values
+ * (rows, letter counts, temperatures) live on the device, and reading them on
+ * the host would synchronise the stream, so the kernel checks them instead: a
+ * decision with a row outside [0, n_rows), n_letters outside [2, min(ld, 255)]
  * (255 = the largest choice question, section 07), or T not a finite positive
- * number gets NaN in every column of both outputs.
+ * number gets NaN in every column of both outputs (the other decisions of the
+ * call are computed normally). T is a per-decision input because the page takes
+ * it per question type from a calibration table the pages do not include
+ * (section 01 "Decision and response", section 02 "Basal protocol").
  * Errors: TA_ERR_INVALID_ARGUMENT, TA_ERR_HIP.
  */
 ta_status decision_readout(const float* logits, int32_t n_rows, int32_t ld, const int32_t* row1,

@@ -193,6 +193,19 @@ def tree_attn_plan(tree, num_q_heads: int, num_kv_heads: int, head_dim: int, sca
     lens = _i32(tree.block_len)
     qb = None if getattr(tree, "row_q_begin", None) is None else _i32(tree.row_q_begin)
     qe = None if getattr(tree, "row_q_end", None) is None else _i32(tree.row_q_end)
+    # The C planner reads these arrays up to the sizes indptr implies; a short
+    # array would be read past its end, so the lengths are checked here.
+    if indptr.ndim != 1 or indptr.shape[0] < 1 or int(indptr[0]) != 0:
+        raise ValueError("row_block_indptr must be a 1-D array starting at 0")
+    if np.any(np.diff(indptr) < 0):
+        raise ValueError("row_block_indptr must be non-decreasing")
+    n_rows, n_blocks = int(indptr.shape[0]) - 1, int(indptr[-1])
+    if parent.shape != (n_blocks,) or lens.shape != (n_blocks,):
+        raise ValueError(f"block_parent and block_len need {n_blocks} entries (row_block_indptr[-1]), "
+                         f"got {parent.shape} and {lens.shape}")
+    for name, a in (("row_q_begin", qb), ("row_q_end", qe)):
+        if a is not None and a.shape != (n_rows,):
+            raise ValueError(f"{name} needs {n_rows} entries (one per row), got {a.shape}")
     desc = _TreeDesc(int(indptr.shape[0]) - 1, _ptr32(indptr), _ptr32(parent), _ptr32(lens),
                      _ptr32(qb), _ptr32(qe))
     od = {"f16": TA_F16, "f32": TA_F32}[out_dtype]

@@ -603,6 +603,11 @@ static ta_status check_cfg(const ta_attn_cfg* c) {
     return fail(TA_ERR_LIMIT, "query heads per KV head = %d; supported: 1, 2, 4, 8", g);
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(TA_ERR_LIMIT, "head_dim %d; supported: 64, 128", c->head_dim);
+  // The kernel forms a key's element offset from the first key of its tile in
+  // 32-bit arithmetic: at most a row (32,768 tokens) times the K/V token stride.
+  if ((int64_t)c->num_kv_heads * c->head_dim * kRowLimit >= ((int64_t)1 << 31))
+    return fail(TA_ERR_LIMIT, "num_kv_heads %d x head_dim %d too large for 32-bit in-row offsets",
+                c->num_kv_heads, c->head_dim);
   if (!(c->scale > 0.0f) || !isfinite(c->scale))
     return fail(TA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
   if (c->out_dtype != TA_F16 && c->out_dtype != TA_F32)

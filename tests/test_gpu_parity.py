@@ -4,7 +4,7 @@ Attention outputs: max-abs <= 2e-3 and relative L2 <= 1e-3 against the oracle
 (the bar stated for this path); decisions: <= 1e-5; plan tables are bit-exact
 (checked on the CPU in test_plan_cpu.py). Small workloads are compared element
 by element; the full-size workloads, in the launch configuration the bench
-times, on sampled query tokens the oracle computes one by one, plus
+times, on every token (seed 0) and on sampled tokens at other seeds, plus
 properties that hold at any size.
 """
 import math
@@ -266,6 +266,44 @@ def test_full_size_sampled(P, cfg, seed):
         assert np.all(np.isfinite(o))
         vmax = float(np.abs(f.v_row).max())
         assert np.abs(o).max() <= vmax + 2e-3
+
+
+def _oracle_every_token(f, wl, block=512):
+    """The f64 oracle on every query token of one forward, in blocks of
+    ``block`` queries run on the host's cores (one BLAS thread per block; the
+    blocks are independent rows of the same definition)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    n = f.q.shape[0]
+    parts = [np.arange(a, min(a + block, n)) for a in range(0, n, block)]
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+
+    def run(sel):
+        return OA.tree_attention(f.tree, f.q, f.k_row, f.v_row, wl.scale, sel=sel, block=block,
+                                 return_lse=True)
+
+    with threadpool_limits(1), ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(run, parts))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res], axis=1)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_full_size_every_token(P, cfg):
+    """Every token and head of the full-size workloads (seed 0), in the launch
+    configuration the bench times, element by element against the oracle; the
+    32k-token row streams its four chunks (later chunks over the cached K/V of
+    earlier ones)."""
+    print(f"[full, every token] config {cfg}", flush=True)
+    wl = W.make_config(cfg, 0)
+    outs, lses, _, _ = run_forwards(P, wl, out_dtype="f16", lse=True)
+    for j, (f, o, l) in enumerate(zip(wl.forwards, outs, lses)):
+        want, want_lse = _oracle_every_token(f, wl)
+        err, rel = _compare(o, want, what=f"O forward {j}")
+        _compare(l, want_lse, atol=LSE_ATOL, rl2=LSE_RL2, what=f"LSE forward {j}")
+        print(f"[full, every token] config {cfg} forward {j}: {o.shape[0]} tokens, "
+              f"max-abs {err:.2e}, rel-L2 {rel:.2e}", flush=True)
 
 
 # ---------------------------------------------------------------------------

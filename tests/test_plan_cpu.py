@@ -118,13 +118,16 @@ def decode_mask_bits(block, n_tok, group, head_dim):
     return (ones > 0).reshape(n_tok, 64)
 
 
-def _expand_schedule(plan, idx, toks):
+def _expand_schedule(plan, idx, toks, block=1024):
     """Apply the kernel's rule to the exported schedule: a tile's query tokens
     see all keys of its unmasked key tiles, and on masked tiles the keys the
     tile's visibility bits allow. The bits are first checked against the rule
     they encode (the tile counts for t, lo <= P(t) < hi, and P(u) <= P(t) <
-    E(u); slots past the tile's keys never). Returns the coverage count per
-    (t, u)."""
+    E(u); slots past the tile's keys never). Yields (t0, t1, cover): the
+    coverage count per (t, u) for the query tokens [t0, t1) of consecutive
+    query tiles holding about ``block`` tokens, so long forwards stream.
+    After the last block, checks that every query token is in exactly one
+    tile and every masked tile has its own block of bits."""
     sch = P.tree_attn_plan_schedule(plan)
     info = plan.info
     masks = P.tree_attn_plan_masks(plan)
@@ -132,33 +135,46 @@ def _expand_schedule(plan, idx, toks):
     assert masks.shape[0] == info["num_masked_key_tiles"] + 1 and not masks[0].any()
     group = plan.cfg["num_q_heads"] // plan.cfg["num_kv_heads"]
     nq, nkv = idx.num_q_tokens, idx.num_kv_tokens
-    cover = np.zeros((nq, nkv), np.int16)
     pre, end = sch["tok_anc"][:, 0], sch["tok_anc"][:, 1]
     seen_q = np.zeros(nq, np.int32)
     blocks = []
-    for qf, qr, n, kb, ke in sch["q_tiles"]:
-        seen_q[qf:qf + n] += 1
-        trows = np.arange(qr, qr + n)
-        for i in range(kb, ke):
-            _, nk, masked, lo, hi, _, _, mblk = sch["key_tiles"][i]
-            keys = key_tile_rows(sch, i)
-            assert len(keys) == nk
-            if masked:
-                pt = pre[trows]
-                rule = ((lo <= pt) & (pt < hi))[:, None] & (pre[keys][None, :] <= pt[:, None]) & \
-                    (pt[:, None] < end[keys][None, :])
-                bits = decode_mask_bits(masks[mblk], n, group, plan.cfg["head_dim"])
-                np.testing.assert_array_equal(bits[:, :nk], rule)
-                assert not bits[:, nk:].any(), "slots past the tile's keys are never visible"
-                vis = bits[:, :nk]
-                blocks.append(int(mblk))
-            else:
-                assert mblk == 0
-                vis = np.ones((n, nk), bool)
-            np.add.at(cover, (slice(qf, qf + n), keys), vis)
+    qt = sch["q_tiles"]
+    order = np.argsort(qt[:, 0], kind="stable")
+    i0 = 0
+    while i0 < len(order):
+        i1 = i0
+        t0 = int(qt[order[i0], 0])
+        while i1 < len(order) and (i1 == i0 or int(qt[order[i1], 0]) + int(qt[order[i1], 2]) - t0 <= block):
+            i1 += 1
+        t1 = int(qt[order[i1 - 1], 0] + qt[order[i1 - 1], 2])
+        assert t1 > t0
+        cover = np.zeros((t1 - t0, nkv), np.int16)
+        for j in order[i0:i1]:
+            qf, qr, n, kb, ke = qt[j]
+            assert t0 <= qf and qf + n <= t1
+            seen_q[qf:qf + n] += 1
+            trows = np.arange(qr, qr + n)
+            for i in range(kb, ke):
+                _, nk, masked, lo, hi, _, _, mblk = sch["key_tiles"][i]
+                keys = key_tile_rows(sch, i)
+                assert len(keys) == nk
+                if masked:
+                    pt = pre[trows]
+                    rule = ((lo <= pt) & (pt < hi))[:, None] & (pre[keys][None, :] <= pt[:, None]) & \
+                        (pt[:, None] < end[keys][None, :])
+                    bits = decode_mask_bits(masks[mblk], n, group, plan.cfg["head_dim"])
+                    np.testing.assert_array_equal(bits[:, :nk], rule)
+                    assert not bits[:, nk:].any(), "slots past the tile's keys are never visible"
+                    vis = bits[:, :nk]
+                    blocks.append(int(mblk))
+                else:
+                    assert mblk == 0
+                    vis = np.ones((n, nk), bool)
+                np.add.at(cover, (slice(qf - t0, qf - t0 + n), keys), vis)
+        yield t0, t1, cover
+        i0 = i1
     assert np.all(seen_q == 1), "every query token in exactly one tile"
     assert sorted(blocks) == list(range(1, len(blocks) + 1)), "one block per masked tile"
-    return sch, cover
 
 
 # blocks of a row listed parents-first but not in pre-order (C's subtree sits
@@ -178,14 +194,14 @@ def test_token_order_encodes_visibility(lib, k):
     else:
         desc, hq, hkv, d = NON_PREORDER, 4, 2, 64
     idx = OT.build_index(desc)
-    if idx.num_q_tokens * idx.num_kv_tokens > 8192 * 9000:
-        pytest.skip("mask too large for this check")
     plan = P.tree_attn_plan(desc, hq, hkv, d, d ** -0.5)
     toks = OT.query_tokens(idx)
     pre, end = P.tree_attn_plan_schedule(plan)["tok_anc"].T
-    tpos = pre[toks["row_pos"]]
-    enc = (pre[None, :] <= tpos[:, None]) & (tpos[:, None] < end[None, :])
-    np.testing.assert_array_equal(enc, OT.dense_mask(idx, toks))
+    for a in range(0, idx.num_q_tokens, 1024):   # query blocks: the long rows stream
+        part = np.arange(a, min(a + 1024, idx.num_q_tokens))
+        tpos = pre[toks["row_pos"][part]]
+        enc = (pre[None, :] <= tpos[:, None]) & (tpos[:, None] < end[None, :])
+        np.testing.assert_array_equal(enc, OT.dense_mask(idx, toks, part))
 
 
 @pytest.mark.parametrize("inv", [False, True], ids=["union", "by-position"])
@@ -193,13 +209,15 @@ def test_token_order_encodes_visibility(lib, k):
 def test_schedule_covers_mask_exactly_once(lib, k, inv):
     name, desc, hq, hkv, d = DESCS[k]
     idx = OT.build_index(desc)
-    if idx.num_q_tokens * idx.num_kv_tokens > 8192 * 9000:
-        pytest.skip("mask too large for this check")  # the long-row chunks
     plan = P.tree_attn_plan(desc, hq, hkv, d, d ** -0.5, batch_invariant=inv)
     toks = OT.query_tokens(idx)
-    sch, cover = _expand_schedule(plan, idx, toks)
-    mask = OT.dense_mask(idx, toks)
-    np.testing.assert_array_equal(cover, mask.astype(np.int16))
+    covered = 0
+    for t0, t1, cover in _expand_schedule(plan, idx, toks):
+        mask = OT.dense_mask(idx, toks, np.arange(t0, t1))
+        np.testing.assert_array_equal(cover, mask.astype(np.int16))
+        covered += t1 - t0
+    assert covered == idx.num_q_tokens
+    sch = P.tree_attn_plan_schedule(plan)
     # unmasked tiles must be full 64-key tiles; tiles never exceed 64 keys
     kt = sch["key_tiles"]
     assert np.all(kt[:, 1] >= 1) and np.all(kt[:, 1] <= 64)
@@ -393,6 +411,29 @@ def test_head_config_errors(lib):
     assert _err(P.tree_attn_plan, ok, 4, 1, 64, 0.0) == 1      # scale
     assert _err(P.tree_attn_plan, ok, 4, 1, 64, float("nan")) == 1
     assert _err(P.tree_attn_plan, ok, 0, 1, 64, 0.1) == 1
+    # in-row key offsets are 32-bit: num_kv_heads * head_dim * 32768 < 2^31
+    assert _err(P.tree_attn_plan, ok, 512, 512, 128, 0.1) == 3
+    assert P.tree_attn_plan(ok, 511, 511, 128, 0.1).info["num_q_tokens"] == 4
+
+
+def test_binding_rejects_short_tree_arrays(lib):
+    """The C planner indexes the block arrays up to row_block_indptr[-1] and the
+    per-row arrays up to num_rows; the binding refuses shorter arrays."""
+    ok = W.desc_from_rows([[(-1, 4), (0, 4)], [(-1, 3)]])
+    short_parent = W.TreeDesc(ok.row_block_indptr, ok.block_parent[:-1], ok.block_len,
+                              ok.row_q_begin, ok.row_q_end)
+    short_len = W.TreeDesc(ok.row_block_indptr, ok.block_parent, ok.block_len[:-1],
+                           ok.row_q_begin, ok.row_q_end)
+    short_qb = W.TreeDesc(ok.row_block_indptr, ok.block_parent, ok.block_len,
+                          ok.row_q_begin[:-1], ok.row_q_end)
+    short_qe = W.TreeDesc(ok.row_block_indptr, ok.block_parent, ok.block_len,
+                          ok.row_q_begin, ok.row_q_end[:-1])
+    decreasing = W.TreeDesc(np.array([0, 2, 1], np.int32), ok.block_parent[:1], ok.block_len[:1],
+                            ok.row_q_begin, ok.row_q_end)
+    for bad in (short_parent, short_len, short_qb, short_qe, decreasing):
+        with pytest.raises(ValueError):
+            P.tree_attn_plan(bad, 4, 1, 64, 0.1)
+    assert P.tree_attn_plan(ok, 4, 1, 64, 0.1).info["num_q_tokens"] == 11
 
 
 def test_forward_needs_upload_and_checks_pointers(lib):
