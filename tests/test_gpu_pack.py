@@ -161,7 +161,10 @@ def test_packed_prompts_match_each_prompt_alone(P, seed, hq, hkv, d, row_cap, ca
         rel = float(np.linalg.norm(diff) / np.linalg.norm(want[sel]))
         assert err <= ATOL and rel <= RL2, f"prompt {i}: max-abs {err:.2e} rel-L2 {rel:.2e}"
     assert seen == set(range(len(fwd_rows))), "every computed token belongs to some prompt"
-    # identical prompts share one readout (the duplicate of prompt 1)
+    # identical prompts in one row share one readout (the duplicate of prompt 1;
+    # prompts join rows in queue order, so under a tight row cap it may land in
+    # a later row and get a readout of its own there)
     dup = len(prompts) - 8
-    assert (pk["prompt_row"][dup], pk["prompt_block"][dup], pk["prompt_readout"][dup]) == \
-        (pk["prompt_row"][1], pk["prompt_block"][1], pk["prompt_readout"][1])
+    if len(lens) == 1 or pk["prompt_row"][dup] == pk["prompt_row"][1]:
+        assert (pk["prompt_row"][dup], pk["prompt_block"][dup], pk["prompt_readout"][dup]) == \
+            (pk["prompt_row"][1], pk["prompt_block"][1], pk["prompt_readout"][1])
