@@ -414,6 +414,29 @@ ta_status readout_mlp(const void* hidden, int64_t n_tokens, const int32_t* reado
                       size_t workspace_bytes, void* h_out, void* hip_stream);
 
 /*
+ * readout_mlp_noalloc -- readout_mlp for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops that must not call
+ * hipMalloc, harnesses that forbid allocation): the same computation, kernels
+ * and results, bit for bit, but no workspace argument. Its scratch (the
+ * workspace layout of readout_mlp) is a fixed 16 MiB array in the library's
+ * device memory, one copy per device, held from the library's first use on
+ * that device until the process ends; the call allocates nothing itself (no
+ * hipMalloc, no allocating library routine). A call needing more than 16 MiB,
+ * i.e. readout_mlp_workspace_size(n_readout, d_model, d_ff) > 16 MiB (at the
+ * Llama-8B and -70B shapes up to 64 readout rows fit), returns TA_ERR_LIMIT
+ * with nothing launched. Every call on one device shares that device's
+ * scratch: calls that may overlap on one device (different streams without
+ * ordering between them, or different host threads) race on it and must be
+ * serialised by the caller; calls on one stream are ordered and safe. The
+ * scratch keeps the last call's contents; every byte a call reads is written
+ * by the same call first. Arguments otherwise as readout_mlp. Errors:
+ * TA_ERR_INVALID_ARGUMENT, TA_ERR_LIMIT (sizes, scratch too small), TA_ERR_HIP.
+ */
+ta_status readout_mlp_noalloc(const void* hidden, int64_t n_tokens, const int32_t* readout_tok,
+                              int32_t n_readout, const ta_mlp_weights* w, void* h_out,
+                              void* hip_stream);
+
+/*
  * letter_logits: the final RMS norm of each readout row and the logits of its
  * answer letters only (rows of the language-model head):
  *   y = f16(h[m] * (mean(h[m]^2) + eps)^(-1/2) * final_norm_w)

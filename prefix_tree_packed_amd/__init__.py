@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     letter_logits,
     load_library,
     readout_mlp,
+    readout_mlp_noalloc,
     readout_mlp_workspace_size,
     readout_pack_gate_up,
     readout_workspace_views,

@@ -30,7 +30,8 @@ EXPORTED = ("tree_attn_plan", "tree_attn_plan_info", "tree_attn_plan_upload",
             "tree_attn_forward_chunked", "tree_attn_cache_write", "tree_attn_rope_cache_write",
             "tree_attn_forward_cached",
             "tree_pack", "tree_pack_info", "tree_pack_export", "tree_pack_destroy",
-            "tree_request_cost", "tree_form_batches", "readout_mlp_workspace_size", "readout_mlp", "readout_pack_gate_up",
+            "tree_request_cost", "tree_form_batches", "readout_mlp_workspace_size", "readout_mlp",
+            "readout_mlp_noalloc", "readout_pack_gate_up",
             "letter_logits", "decision_readout", "tree_attn_mfma_peak_probe", "tree_attn_last_error")
 
 
@@ -122,6 +123,7 @@ def load_library(path: str = LIB_PATH):
     lib.tree_form_batches.argtypes = [p64, i32, i64, p32]
     lib.readout_mlp_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.readout_mlp.argtypes = [vp, i64, vp, i32, ctypes.POINTER(_MlpWeights), vp, ctypes.c_size_t, vp, vp]
+    lib.readout_mlp_noalloc.argtypes = [vp, i64, vp, i32, ctypes.POINTER(_MlpWeights), vp, vp]
     lib.readout_pack_gate_up.argtypes = [vp, vp, i32, i32, vp, vp]
     lib.tree_attn_mfma_peak_probe.argtypes = [i32, i32, vp, ctypes.POINTER(ctypes.c_int64), vp]
     lib.letter_logits.argtypes = [vp, i32, i32, vp, ctypes.c_float, vp, i32, vp, vp, i32, vp, vp]
@@ -495,6 +497,29 @@ def readout_mlp(hidden, readout_tok, norm_w, w_gate_up, w_down, h_out, eps: floa
                                       _vp(workspace), int(workspace.numel()), _vp(h_out),
                                       _stream_handle(stream)))
     return workspace
+
+
+def readout_mlp_noalloc(hidden, readout_tok, norm_w, w_gate_up, w_down, h_out, eps: float = 1e-5,
+                        stream=None) -> None:
+    """readout_mlp without a workspace: the library's fixed per-device scratch
+    holds the intermediates (for callers that cannot allocate; calls that may
+    overlap on one device race on that scratch)."""
+    import torch
+    if hidden.dim() != 2:
+        raise ValueError("hidden must be [n_tokens, d_model]")
+    n_tok, dm = hidden.shape
+    ff = w_gate_up.shape[0] // 2
+    n = readout_tok.shape[0]
+    _expect(hidden, "hidden", (n_tok, dm), torch.float16)
+    _expect(readout_tok, "readout_tok", (n,), torch.int32)
+    _expect(norm_w, "norm_w", (dm,), torch.float16)
+    _expect(w_gate_up, "w_gate_up", (2 * ff, dm), torch.float16)
+    _expect(w_down, "w_down", (dm, ff), torch.float16)
+    _expect(h_out, "h_out", (n, dm), torch.float16)
+    w = _MlpWeights(int(dm), int(ff), float(eps), 0, norm_w.data_ptr(), w_gate_up.data_ptr(),
+                    w_down.data_ptr())
+    _check(load_library().readout_mlp_noalloc(_vp(hidden), int(n_tok), _vp(readout_tok), int(n),
+                                              ctypes.byref(w), _vp(h_out), _stream_handle(stream)))
 
 
 def letter_logits(h, final_norm_w, lm_head, letter_ids, n_letters, logits, eps: float = 1e-5,

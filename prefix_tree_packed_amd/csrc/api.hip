@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -246,6 +247,38 @@ static ReadoutLayout readout_layout(int n, int d_model, int d_ff) {
   return l;
 }
 
+// Device scratch of readout_mlp_noalloc: the readout_mlp workspace layout
+// (normalized rows, activations, the down product's partial sums) in a
+// file-scope array instead of a caller's buffer. Each device holds its own
+// copy from the moment the library's code is loaded on it until the process
+// ends. Its address is looked up once per device (hipGetSymbolAddress) and
+// only that address is handed to kernels: in host code the array's name is a
+// host-side stand-in, not a device address.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+static unsigned char* g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch`, looked up on the device's first call.
+static ta_status device_scratch(unsigned char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(TA_ERR_LIMIT, "device index %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(TA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = (unsigned char*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TA_OK;
+}
+
 static ta_status check_mlp_shape(int32_t n, int32_t d_model, int32_t d_ff) {
   if (n < 0) return fail(TA_ERR_INVALID_ARGUMENT, "n_readout %d < 0", n);
   if (d_model < 256 || d_model > kReadoutMaxModel || d_model % 256)
@@ -268,28 +301,44 @@ ta_status readout_mlp_workspace_size(int32_t n_readout, int32_t d_model, int32_t
   return TA_OK;
 }
 
-ta_status readout_mlp(const void* hidden, int64_t n_tokens, const int32_t* readout_tok,
-                      int32_t n_readout, const ta_mlp_weights* w, void* workspace,
-                      size_t workspace_bytes, void* h_out, void* hip_stream) {
-  ta::clear_error();
-  if (!w) return ta::fail(TA_ERR_INVALID_ARGUMENT, "NULL weights");
-  ta_status st = ta::check_mlp_shape(n_readout, w->d_model, w->d_ff);
+}  // extern "C"
+
+namespace ta {
+
+// readout_mlp's argument checks and launches; `workspace` is the caller's
+// buffer or this device's scratch (noalloc: sizes beyond it are refused).
+static ta_status readout_mlp_impl(const void* hidden, int64_t n_tokens, const int32_t* readout_tok,
+                                  int32_t n_readout, const ta_mlp_weights* w, void* workspace,
+                                  size_t workspace_bytes, void* h_out, void* hip_stream, bool noalloc) {
+  if (!w) return fail(TA_ERR_INVALID_ARGUMENT, "NULL weights");
+  ta_status st = check_mlp_shape(n_readout, w->d_model, w->d_ff);
   if (st != TA_OK) return st;
   if (n_readout == 0) return TA_OK;
-  if (n_tokens < 1) return ta::fail(TA_ERR_INVALID_ARGUMENT, "n_tokens %lld < 1", (long long)n_tokens);
-  if (!(w->eps >= 0.f)) return ta::fail(TA_ERR_INVALID_ARGUMENT, "eps must be >= 0");
+  if (n_tokens < 1) return fail(TA_ERR_INVALID_ARGUMENT, "n_tokens %lld < 1", (long long)n_tokens);
+  if (!(w->eps >= 0.f)) return fail(TA_ERR_INVALID_ARGUMENT, "eps must be >= 0");
+  const ReadoutLayout l = readout_layout(n_readout, w->d_model, w->d_ff);
+  if (noalloc) {
+    if (l.total > kNoAllocScratchBytes)
+      return fail(TA_ERR_LIMIT,
+                  "readout_mlp_noalloc: %d rows at d_model %d, d_ff %d need %zu bytes of scratch, "
+                  "more than its fixed %zu; pass a workspace to readout_mlp instead",
+                  n_readout, w->d_model, w->d_ff, l.total, kNoAllocScratchBytes);
+    unsigned char* sp = nullptr;
+    st = device_scratch(&sp);
+    if (st != TA_OK) return st;
+    workspace = sp;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   const void* ptrs[] = {hidden, readout_tok, w->norm_w, w->w_gate_up, w->w_down, workspace, h_out};
   const char* names[] = {"hidden", "readout_tok", "norm_w", "w_gate_up", "w_down", "workspace", "h_out"};
   for (int i = 0; i < 7; ++i) {
-    if (!ptrs[i]) return ta::fail(TA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
-    if (!ta::aligned16(ptrs[i]))
-      return ta::fail(TA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+    if (!ptrs[i]) return fail(TA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(TA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
   }
-  const ta::ReadoutLayout l = ta::readout_layout(n_readout, w->d_model, w->d_ff);
   if (workspace_bytes < l.total)
-    return ta::fail(TA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, l.total);
+    return fail(TA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, l.total);
   unsigned char* ws = (unsigned char*)workspace;
-  ta::ReadoutArgs a;
+  ReadoutArgs a;
   a.hidden = hidden;
   a.n_tokens = n_tokens;
   a.readout_tok = readout_tok;
@@ -305,9 +354,29 @@ ta_status readout_mlp(const void* hidden, int64_t n_tokens, const int32_t* reado
   a.d_ff = w->d_ff;
   a.splits = l.splits;
   a.eps = w->eps;
-  hipError_t e = ta::launch_readout_mlp(a, (hipStream_t)hip_stream);
-  if (e != hipSuccess) return ta::hip_fail(e, "readout MLP launch");
+  hipError_t e = launch_readout_mlp(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "readout MLP launch");
   return TA_OK;
+}
+
+}  // namespace ta
+
+extern "C" {
+
+ta_status readout_mlp(const void* hidden, int64_t n_tokens, const int32_t* readout_tok,
+                      int32_t n_readout, const ta_mlp_weights* w, void* workspace,
+                      size_t workspace_bytes, void* h_out, void* hip_stream) {
+  ta::clear_error();
+  return ta::readout_mlp_impl(hidden, n_tokens, readout_tok, n_readout, w, workspace, workspace_bytes,
+                              h_out, hip_stream, false);
+}
+
+ta_status readout_mlp_noalloc(const void* hidden, int64_t n_tokens, const int32_t* readout_tok,
+                              int32_t n_readout, const ta_mlp_weights* w, void* h_out,
+                              void* hip_stream) {
+  ta::clear_error();
+  return ta::readout_mlp_impl(hidden, n_tokens, readout_tok, n_readout, w, nullptr, 0, h_out,
+                              hip_stream, true);
 }
 
 ta_status readout_pack_gate_up(const void* w_gate, const void* w_up, int32_t d_ff, int32_t d_model,
