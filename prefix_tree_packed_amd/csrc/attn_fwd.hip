@@ -25,10 +25,12 @@
 //                   of the S^T accumulators, loaded into LDS with the tile,
 //                   and a set bit keeps the score, a clear one makes it -inf
 //                   (two VALU ops per score)
-//   softmax         one running reference max per column (two cross-lane steps
-//                   over the 4 lane groups that share a column), moved only
-//                   when a score exceeds it by 2^8; exp2 with log2(e) folded
-//                   into the scale
+//   softmax         one running reference per column, set from the column max
+//                   of an item's first tile (two cross-lane steps over the 4
+//                   lane groups that share a column) and moved only when a
+//                   score exceeds it by 2^8, which the kernel detects from the
+//                   f16 probabilities themselves (a probability >= 256); exp2
+//                   with log2(e) folded into the scale
 //   O^T += V^T P^T  A = V^T read transposed out of row-major LDS
 //                   (ds_read_b64_tr_b16), B = P^T straight from the S^T
 //                   accumulators rounded to f16; the row sums of that P come
@@ -453,19 +455,63 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     }
   };
 
+  // The reference check of a tile. Its probabilities were computed against the
+  // running reference m of their column. The reference must move when the
+  // tile's column max exceeds m by more than kRescaleSlack, and then some
+  // probability of that column is >= 2^kRescaleSlack = 256 (an overflow to
+  // infinity included). The exact maximum of the lane's f16 probabilities
+  // (packed 3-input maxima) tests for that; only when it is reached anywhere
+  // in the wave is the tile's exact column max taken from its scores, and a
+  // column whose max exceeds its reference by more than the slack moves it
+  // there: O and the row sums, which hold the earlier tiles, are rescaled and
+  // the probabilities recomputed. The move depends on the column's own
+  // scores only, so padded columns that mirror a token compute exactly what
+  // that token's column computes.
+  auto check_reference = [&](const f4 (&sc)[4][NCG], h8 (&pb)[2][NCG]) {
+    h2 m = h2{(_Float16)0.f, (_Float16)0.f};
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
+        // element pairs, the packed dwords the P.V product reads (read by
+        // element: a bit_cast of this vector has been folded to partly
+        // undefined lanes by the optimizer)
+        const h8& q = pb[kc][cg];
+        m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, h2{q[0], q[1]}), h2{q[2], q[3]});
+        m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, h2{q[4], q[5]}), h2{q[6], q[7]});
+      }
+    const _Float16 big = (_Float16)(float)(1 << (int)kRescaleSlack);
+    if (__builtin_expect(__any(m[0] >= big || m[1] >= big), 0)) {
+      float mx[NCG], mnew[NCG];
+      tile_max_raw(sc, mx);
+      bool need_any = false;
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
+        const float ms = mx[cg] * scale_log2e;
+        const bool need = ms > mrun[cg] + kRescaleSlack;
+        mnew[cg] = need ? ms : mrun[cg];
+        need_any |= need;
+      }
+      if (__any(need_any)) {
+        rescale(need_any, mnew);
+        probs(sc, pb);
+      }
+    }
+  };
+
   // Software pipeline. Step kt runs one hand-ordered block: the scores of
   // tile kt+1 (K fragments read two sub-steps ahead, NCG MFMAs per fragment)
-  // with the probabilities of tile kt spread between them, then the P.V
-  // product of tile kt (V^T fragments read two sub-steps ahead) with the raw
-  // max of tile kt+1 spread between its MFMAs. Fences keep the compiler from
-  // hoisting every LDS read (which costs registers) or clustering the VALU
-  // work away from the MFMAs. After the block, tile kt+1 is masked if flagged
-  // (its max retaken) and the reference moves (rescaling O, which by then
-  // holds tile kt), so tile kt+1's probabilities need no branch. Tile kt+3's
-  // loads are issued at the start; K(kt+1) and V(kt) are read, so four stages
-  // keep every live tile resident. (Unrolling by two so the two score buffers
-  // swap roles instead of being copied runs out of registers; the copy mostly
-  // coalesces away.)
+  // with the probabilities of tile kt spread between them, the reference
+  // check of tile kt (a branch taken only when some probability reached the
+  // slack), then the P.V product of tile kt (V^T fragments read two
+  // sub-steps ahead). Fences keep the compiler from hoisting every LDS read
+  // (which costs registers) or clustering the VALU work away from the MFMAs.
+  // After the block, tile kt+1 is masked if flagged. No column max is taken
+  // per tile: the check replaces it (about a quarter of the VALU work per step
+  // before it). Tile kt+3's loads are issued at the start; K(kt+1) and V(kt)
+  // are read, so four stages keep every live tile resident. (Unrolling by two
+  // so the two score buffers swap roles instead of being copied runs out of
+  // registers; the copy mostly coalesces away.)
   constexpr int KPF = TA_KPF;                // K fragments read ahead of their S sub-step
   constexpr int VPF = TA_VPF;                // V^T fragments read ahead of their P.V sub-step
   static_assert(KPF >= 1 && VPF >= 1 && VPF <= 4 * DC, "read-ahead distances");
@@ -473,18 +519,13 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   constexpr int NE = 16 * NCG;               // probabilities per lane per tile
   constexpr int EPS = (NE + NA - 1) / NA;    // of them per S sub-step
   constexpr int NB = 2 * DT;                 // P.V sub-steps: one V^T fragment each
-  constexpr int NM = 4 * NCG;                // raw-max partials per lane
-  constexpr int MPS = (NM + NB - 3) / (NB - 2);  // of them per P.V sub-step from the third
-  static_assert(NB > 2 && (NB - 2) * MPS >= NM, "max partials fit");
 
-  auto fused = [&](int sk, int sv, const f4 (&cur)[4][NCG], f4 (&nxt)[4][NCG],
-                   float (&mraw)[NCG]) {
+  auto fused = [&](int sk, int sv, const f4 (&cur)[4][NCG], f4 (&nxt)[4][NCG]) {
     const unsigned char* kl = lds.k[sk];
     const unsigned char* vl = lds.v[sv];
     h8 kf[NA];
     s4v vlo[NB], vhi[NB];
     h8 pb[2][NCG];
-    float mpart[NCG];
     // sub-step i reads key rows 16*(i / DC) .. +15, head-dim chunk i % DC: one
     // row block's accumulators complete before the next starts, so the next
     // tile's scores grow while this tile's are consumed
@@ -516,7 +557,13 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
       for (int j = 0; j < VPF; ++j)
         if (i == NA - VPF + j) vread(j);
 #pragma unroll
-      for (int e = i * EPS; e < (i + 1) * EPS && e < NE; ++e) prob(e);
+      for (int e = i * EPS; e < (i + 1) * EPS && e < NE; ++e) {
+        prob(e);
+        // a completed f16 operand is materialised here, inside the sub-step
+        // (otherwise its conversions may sink to the reference check after
+        // the score phase, away from the MFMAs they overlap)
+        if (e % 8 == 7) asm volatile("" ::"v"(pb[(e >> 3) / NCG][(e >> 3) % NCG]));
+      }
       const int ks = i / DC, dc = i % DC;
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg)
@@ -525,6 +572,8 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
+    // probabilities against the reference; refit if some exceed the slack
+    check_reference(cur, pb);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (j + VPF < NB) vread(j + VPF);
@@ -540,36 +589,10 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg)
         oacc[dt][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[kc][cg], oacc[dt][cg], 0, 0, 0);
-      // raw max partials of the next tile's scores (its MFMAs have drained)
-#pragma unroll
-      for (int q = (j - 2) * MPS; q >= 0 && q < (j - 1) * MPS && q < NM; ++q) {
-        const int ks = q % 4, cg = q / 4;
-        const f4 x = nxt[ks][cg];
-        mpart[cg] = ks == 0 ? max3f(x[0], x[1], fmaxf(x[2], x[3]))
-                            : max3f(mpart[cg], max3f(x[0], x[1], x[2]), x[3]);
-      }
-      if (j == NB - 1) {
-#pragma unroll
-        for (int cg = 0; cg < NCG; ++cg) mraw[cg] = column_max(mpart[cg]);
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // moves the reference to a tile's column max (already reduced over the
-  // column's lanes) when a score exceeds it by kRescaleSlack
-  auto move_reference = [&](const float (&mx)[NCG]) {
-    float mnew[NCG];
-    bool need_any = false;
-#pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) {
-      const float ms = mx[cg] * scale_log2e;
-      const bool need = ms > mrun[cg] + kRescaleSlack;
-      mnew[cg] = need ? ms : mrun[cg];
-      need_any |= need;
-    }
-    rescale(need_any, mnew);
-  };
 
   int s = 0;  // stage of the tile being consumed
   // The end of every consumed tile: the tile two places further on must have
@@ -596,20 +619,12 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     const int s1 = (s + 1) & (kStages - 1);
     const bool issued = issue_next();
 
-    float mx[NCG];
-    fused(s1, s, cur, nxt, mx);
+    fused(s1, s, cur, nxt);
 
     const bool masked = c_meta & kMaskedBit;
     if (kt + 2 < kte) c_meta = ktiles[kt + 2].meta;
     l_fetch();
-    if (masked) {
-      apply_mask(s1, nxt);
-      float m[NCG];
-      tile_max_raw(nxt, m);
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) mx[cg] = m[cg];
-    }
-    move_reference(mx);
+    if (masked) apply_mask(s1, nxt);
     end_of_tile(issued);
   };
 
@@ -658,6 +673,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     {
       h8 pb[2][NCG];
       probs(sa, pb);
+      check_reference(sa, pb);
       pv_product(s, pb);
     }
     if (!last) end_of_tile(issued);
