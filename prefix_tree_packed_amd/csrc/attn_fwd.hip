@@ -18,6 +18,9 @@
 // Per 64-key tile (four LDS stages; a tile's loads are issued three tiles
 // ahead of its P.V product, straight from global memory into LDS):
 //   S^T = K Q^T     v_mfma_f32_16x16x32_f16, A = K rows from LDS, B = Q
+//                   scaled by scale * log2(e) once per item; each score chain
+//                   starts from minus the column's softmax reference, so the
+//                   accumulators hold scores relative to it in log2 units
 //   mask            only on tiles the plan flags: key u is visible to query t
 //                   iff u's block is a proper ancestor of t's block or the
 //                   same block with u <= t (and the tile counts for t); the
@@ -26,11 +29,12 @@
 //                   and a set bit keeps the score, a clear one makes it -inf
 //                   (two VALU ops per score)
 //   softmax         one running reference per column, set from the column max
-//                   of an item's first tile (two cross-lane steps over the 4
-//                   lane groups that share a column) and moved only when a
-//                   score exceeds it by 2^8, which the kernel detects from the
-//                   f16 probabilities themselves (a probability >= 256); exp2
-//                   with log2(e) folded into the scale
+//                   of the item's first tile holding a key the column sees
+//                   (two cross-lane steps over the 4 lane groups that share a
+//                   column) and moved only when a score exceeds it by 2^8,
+//                   which the kernel detects from the f16 probabilities
+//                   themselves (a probability >= 256); a probability is one
+//                   exp2 of the accumulator, no multiply-add
 //   O^T += V^T P^T  A = V^T read transposed out of row-major LDS
 //                   (ds_read_b64_tr_b16), B = P^T straight from the S^T
 //                   accumulators rounded to f16; the row sums of that P come
@@ -148,6 +152,11 @@ template <int DCH>
 __device__ __forceinline__ int v_swizzle(int r) {
   return ((2 * (r & 3)) | (((r >> 2) & 1) << 3)) & (DCH - 1);
 }
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding and leaves the other counters alone (gfx9 encoding).
@@ -325,7 +334,16 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   open_item(ib);
 
   f4 oacc[DT][NCG];
+  // mrun: the column's softmax reference (log2 units); negm: -mrun in the
+  // layout of an S^T accumulator, the value every score chain starts from, so
+  // the accumulators hold scores relative to the reference; fresh: the column
+  // has not seen a key of the item yet (its O and row sum are still zero, and
+  // its reference is only a placeholder); any_fresh: some column of the wave is
+  // fresh
   float mrun[NCG];
+  f4 negm[NCG];
+  bool fresh[NCG];
+  bool any_fresh = true;
   f4 lacc[NCG];
   const _Float16 one = (_Float16)1.0f;
   const h8 ones = h8{one, one, one, one, one, one, one, one};
@@ -350,13 +368,26 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   wait_vmcnt<0>();
   __syncthreads();
 
-  // S^T of one key tile: K rows from LDS (A) against the Q fragments (B)
+  // The softmax scale and log2(e) go into Q once per item: each Q element is
+  // multiplied in f32 and rounded to f16 once, so the scores come out of the
+  // MFMAs in log2 units and the exponentials need no multiply.
+  auto scale_q = [&]() {
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[cg][dc][i] = (_Float16)((float)qf[cg][dc][i] * scale_log2e);
+  };
+
+  // S^T of one key tile: K rows from LDS (A) against the Q fragments (B),
+  // relative to the reference
   auto s_product = [&](int stage, f4 (&sacc)[4][NCG]) {
     const unsigned char* kl = lds.k[stage];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) sacc[ks][cg] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int cg = 0; cg < NCG; ++cg) sacc[ks][cg] = negm[cg];
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
 #pragma unroll
@@ -403,22 +434,49 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     }
   };
 
-  // O and the row sums move to the new reference max (rare)
-  auto rescale = [&](bool need_any, const float (&mnew)[NCG]) {
-    if (__any(need_any)) {
+  // Moves the references (rare). sc holds a tile's scores relative to the
+  // references. A column that has seen a key moves its reference up by its
+  // tile max d when d exceeds the slack, and its O and row sum are rescaled by
+  // 2^-d; a fresh column takes its tile max as its first reference as soon as
+  // the tile holds a key it sees (nothing to rescale). The tile's scores, and
+  // those of the next tile when nx is given (already accumulated against the
+  // old reference), shift by -d. Returns whether any reference of the wave moved.
+  auto refit = [&](auto with_next, f4 (&sc)[4][NCG], f4 (&nx)[4][NCG]) {
+    float mx[NCG];
+    tile_max_raw(sc, mx);
+    float d[NCG];
+    bool moved = false;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      const bool seen = mx[cg] != -__builtin_inff();
+      const bool mv = fresh[cg] ? seen : mx[cg] > kRescaleSlack;
+      d[cg] = mv ? mx[cg] : 0.f;
+      const float alpha = fresh[cg] ? 1.f : __builtin_amdgcn_exp2f(-d[cg]);
+      fresh[cg] = fresh[cg] && !seen;
+      moved |= mv;
+      mrun[cg] += d[cg];
+      negm[cg] = f4{-mrun[cg], -mrun[cg], -mrun[cg], -mrun[cg]};
+      lacc[cg] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt][cg] *= alpha;
+    }
+    bool fr = false;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) fr |= fresh[cg];
+    any_fresh = __any(fr);
+    if (!__any(moved)) return false;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
-        const float alpha = __builtin_amdgcn_exp2f(mrun[cg] - mnew[cg]);
-        mrun[cg] = mnew[cg];
-        lacc[cg] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt][cg] *= alpha;
+        sc[ks][cg] -= d[cg];
+        if constexpr (decltype(with_next)::value) nx[ks][cg] -= d[cg];
       }
-    }
+    return true;
   };
 
-  // P = exp2(s * scale * log2(e) - reference), rounded to f16 in the B-operand
-  // layout of the P.V product
+  // P = exp2(score - reference), rounded to f16 in the B-operand layout of the
+  // P.V product
   auto probs = [&](const f4 (&sacc)[4][NCG], h8 (&pb)[2][NCG]) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
@@ -428,8 +486,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            pb[kc][cg][k2 * 4 + r] = (_Float16)__builtin_amdgcn_exp2f(
-                __builtin_fmaf(sacc[2 * kc + k2][cg][r], scale_log2e, -mrun[cg]));
+            pb[kc][cg][k2 * 4 + r] = (_Float16)__builtin_amdgcn_exp2f(sacc[2 * kc + k2][cg][r]);
   };
 
   // O^T += V^T P^T, row sums += 1^T P^T
@@ -455,19 +512,18 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     }
   };
 
-  // The reference check of a tile. Its probabilities were computed against the
-  // running reference m of their column. The reference must move when the
-  // tile's column max exceeds m by more than kRescaleSlack, and then some
-  // probability of that column is >= 2^kRescaleSlack = 256 (an overflow to
-  // infinity included). The exact maximum of the lane's f16 probabilities
-  // (packed 3-input maxima) tests for that; only when it is reached anywhere
-  // in the wave is the tile's exact column max taken from its scores, and a
-  // column whose max exceeds its reference by more than the slack moves it
-  // there: O and the row sums, which hold the earlier tiles, are rescaled and
-  // the probabilities recomputed. The move depends on the column's own
-  // scores only, so padded columns that mirror a token compute exactly what
-  // that token's column computes.
-  auto check_reference = [&](const f4 (&sc)[4][NCG], h8 (&pb)[2][NCG]) {
+  // The reference check of a tile. Its scores are relative to the running
+  // reference m of their column. The reference must move when the tile's
+  // column max exceeds m by more than kRescaleSlack, and then some probability
+  // of that column is >= 2^kRescaleSlack = 256 (an overflow to infinity
+  // included). The exact maximum of the lane's f16 probabilities (packed
+  // 3-input maxima) tests for that; only when it is reached anywhere in the
+  // wave, or while some column is fresh, does refit take the tile's exact
+  // column max and move the references that need it (the probabilities are
+  // then recomputed). A move depends on the column's own scores only, so
+  // padded columns that mirror a token compute exactly what that token's
+  // column computes.
+  auto check_reference = [&](auto with_next, f4 (&sc)[4][NCG], h8 (&pb)[2][NCG], f4 (&nx)[4][NCG]) {
     h2 m = h2{(_Float16)0.f, (_Float16)0.f};
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
@@ -481,21 +537,8 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
         m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, h2{q[4], q[5]}), h2{q[6], q[7]});
       }
     const _Float16 big = (_Float16)(float)(1 << (int)kRescaleSlack);
-    if (__builtin_expect(__any(m[0] >= big || m[1] >= big), 0)) {
-      float mx[NCG], mnew[NCG];
-      tile_max_raw(sc, mx);
-      bool need_any = false;
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) {
-        const float ms = mx[cg] * scale_log2e;
-        const bool need = ms > mrun[cg] + kRescaleSlack;
-        mnew[cg] = need ? ms : mrun[cg];
-        need_any |= need;
-      }
-      if (__any(need_any)) {
-        rescale(need_any, mnew);
-        probs(sc, pb);
-      }
+    if (__builtin_expect(__any(m[0] >= big || m[1] >= big) || any_fresh, 0)) {
+      if (refit(with_next, sc, nx)) probs(sc, pb);
     }
   };
 
@@ -520,7 +563,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   constexpr int EPS = (NE + NA - 1) / NA;    // of them per S sub-step
   constexpr int NB = 2 * DT;                 // P.V sub-steps: one V^T fragment each
 
-  auto fused = [&](int sk, int sv, const f4 (&cur)[4][NCG], f4 (&nxt)[4][NCG]) {
+  auto fused = [&](int sk, int sv, f4 (&cur)[4][NCG], f4 (&nxt)[4][NCG]) {
     const unsigned char* kl = lds.k[sk];
     const unsigned char* vl = lds.v[sv];
     h8 kf[NA];
@@ -540,8 +583,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     // probability e: key chunk kc, column group cg, half k2, element r
     auto prob = [&](int e) {
       const int r = e & 3, k2 = (e >> 2) & 1, cg = (e >> 3) % NCG, kc = (e >> 3) / NCG;
-      pb[kc][cg][k2 * 4 + r] = (_Float16)__builtin_amdgcn_exp2f(
-          __builtin_fmaf(cur[2 * kc + k2][cg][r], scale_log2e, -mrun[cg]));
+      pb[kc][cg][k2 * 4 + r] = (_Float16)__builtin_amdgcn_exp2f(cur[2 * kc + k2][cg][r]);
     };
     // The wave in its score phase gets issue priority over the other wave on
     // its SIMD, which is then more often in its P.V phase or between tiles:
@@ -568,12 +610,12 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg)
         nxt[ks][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            kf[i], qf[cg][dc], dc == 0 ? f4{0.f, 0.f, 0.f, 0.f} : nxt[ks][cg], 0, 0, 0);
+            kf[i], qf[cg][dc], dc == 0 ? negm[cg] : nxt[ks][cg], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
     // probabilities against the reference; refit if some exceed the slack
-    check_reference(cur, pb);
+    check_reference(BoolC<true>{}, cur, pb, nxt);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (j + VPF < NB) vread(j + VPF);
@@ -615,7 +657,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   };
   // c_meta: meta of the compute cursor's next tile (kt + 1), read a step ahead
   int c_meta = 0;
-  auto step = [&](int kt, int kte, const f4 (&cur)[4][NCG], f4 (&nxt)[4][NCG]) {
+  auto step = [&](int kt, int kte, f4 (&cur)[4][NCG], f4 (&nxt)[4][NCG]) {
     const int s1 = (s + 1) & (kStages - 1);
     const bool issued = issue_next();
 
@@ -632,9 +674,12 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   for (int pos = ib;;) {
     // ---- item `pos`: Q fragments and columns are loaded -------------------
     const int ktb = tile.kt_begin, kte = tile.kt_end;
+    scale_q();
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
-      mrun[cg] = -1e30f;
+      mrun[cg] = 0.f;
+      negm[cg] = f4{0.f, 0.f, 0.f, 0.f};
+      fresh[cg] = true;
       lacc[cg] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[dt][cg] = f4{0.f, 0.f, 0.f, 0.f};
@@ -644,13 +689,9 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
       if (ktb + 1 < kte) c_meta = ktiles[ktb + 1].meta;
       s_product(s, sa);
       if (meta0 & kMaskedBit) apply_mask(s, sa);
-      // the first reference is the tile's own column max (O and the row sums
-      // are still zero, so nothing is rescaled); a column that sees none of
-      // the tile's keys keeps a finite floor
-      float mx[NCG];
-      tile_max_raw(sa, mx);
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) mrun[cg] = fmaxf(mx[cg] * scale_log2e, -1e30f);
+      // every column starts fresh: the first reference is the column's max
+      // over the first tile that holds a key it sees
+      refit(BoolC<false>{}, sa, sa);
     }
     for (int kt = ktb; kt + 1 < kte; ++kt) {
       step(kt, kte, sa, sb);
@@ -673,7 +714,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     {
       h8 pb[2][NCG];
       probs(sa, pb);
-      check_reference(sa, pb);
+      check_reference(BoolC<false>{}, sa, pb, sa);
       pv_product(s, pb);
     }
     if (!last) end_of_tile(issued);
