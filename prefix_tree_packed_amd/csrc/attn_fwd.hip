@@ -105,7 +105,7 @@ __device__ __forceinline__ float column_max(float x) {
 #define TA_KPF 2
 #endif
 #ifndef TA_VPF
-#define TA_VPF 2
+#define TA_VPF 3
 #endif
 
 // LDS stages: a tile's loads are issued three tiles ahead of its P.V product
@@ -537,7 +537,8 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
         m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, h2{q[4], q[5]}), h2{q[6], q[7]});
       }
     const _Float16 big = (_Float16)(float)(1 << (int)kRescaleSlack);
-    if (__builtin_expect(__any(m[0] >= big || m[1] >= big) || any_fresh, 0)) {
+    const _Float16 mm = __builtin_elementwise_maximum(m[0], m[1]);
+    if (__builtin_expect(__any(mm >= big) || any_fresh, 0)) {
       if (refit(with_next, sc, nx)) probs(sc, pb);
     }
   };
