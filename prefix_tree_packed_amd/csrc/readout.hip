@@ -26,11 +26,11 @@
 // weight rows as the A operand (8 consecutive K values per lane, streamed from
 // global memory through a register ring several steps deep) and the
 // activation rows as the B operand (staged in LDS, shared by the eight waves).
-// Each output is one wave's MFMA chain over its K range in K order, and the
-// down product's K splits are fixed by the weight shape and summed in split
-// order, so nothing in a row's arithmetic depends on how many rows are in the
-// call or where the row sits: letter logits are bitwise identical alone or in
-// a batch.
+// Each output is one wave's MFMA chain over its K range (in an order fixed by
+// the output's column block), and the down product's K splits are fixed by
+// the weight shape and summed in split order, so nothing in a row's
+// arithmetic depends on how many rows are in the call or where the row sits:
+// letter logits are bitwise identical alone or in a batch.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
@@ -124,7 +124,7 @@ readout_norm_kernel(const _Float16* __restrict__ hidden, long long n_tokens,
 // One workgroup: WAVES * 16 weight rows, 16 per wave (one MFMA A fragment), against
 // one pass of MF*16 activation rows (the B fragments), over the K range
 // [split * k_len, (split + 1) * k_len). Every output is one wave's MFMA chain
-// over that range in K order.
+// over that range, 256-deep K stages starting at a stage fixed by the unit.
 //   GATE_UP: w0 is the interleaved gate/up matrix (16-row blocks: gate rows
 //            8i .. 8i+7, then the up rows of the same columns); wave w streams
 //            block WAVES*unit + w, so its fragment rows 0-7 are gate rows
@@ -175,6 +175,13 @@ mlp_mfma_kernel(const _Float16* __restrict__ x, int ldx,  // activations [n_rows
   const int kb = split * k_len;
   const int nstages = k_len / kSlice;
   const int nsteps = nstages * kSteps;
+  // Each unit walks its K range starting at its own stage and wrapping
+  // around: units that start together then read different K offsets of their
+  // rows instead of the same offset of rows a power-of-two stride apart, which
+  // piles the requests onto a few HBM channels (measured at d_model 8192: 13%
+  // faster). The order depends on the unit only, never on the rows in the call.
+  const int rot = (unit * 5) % nstages;
+  auto kstage = [&](int s) { return s + rot < nstages ? s + rot : s + rot - nstages; };
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
 
   // WROWS consecutive weight rows per workgroup, 16 per wave
@@ -199,7 +206,7 @@ mlp_mfma_kernel(const _Float16* __restrict__ x, int ldx,  // activations [n_rows
     h8 xr[2][XCH];
     auto xload = [&](int set, int stage) {
 #pragma unroll
-      for (int i = 0; i < XCH; ++i) xr[set][i] = *(const h8*)(xsrc[i] + stage * kSlice);
+      for (int i = 0; i < XCH; ++i) xr[set][i] = *(const h8*)(xsrc[i] + kstage(stage) * kSlice);
     };
     auto xstore = [&](int set, int buf) {
 #pragma unroll
@@ -208,8 +215,9 @@ mlp_mfma_kernel(const _Float16* __restrict__ x, int ldx,  // activations [n_rows
 
     h8 wr[kRing][2];
     auto wload = [&](int slot, int step) {
+      const int k = (kstage(step / kSteps) * kSteps + step % kSteps) * kStepK;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) wr[slot][ks] = *(const h8*)(wp + step * kStepK + ks * 32);
+      for (int ks = 0; ks < 2; ++ks) wr[slot][ks] = *(const h8*)(wp + k + ks * 32);
     };
     f4 acc[MF];
 #pragma unroll
