@@ -273,7 +273,8 @@ ta_status tree_attn_plan_destroy(ta_plan_t plan);
  *   o   [T_q, Hq, D] out_dtype  lse  [Hq, T_q] f32 natural-log sum-exp, or NULL
  * O[t,h] = sum_u P[t,u] V[u,kv] with P the softmax over the keys u that t may
  * see of scale * Q[t,h].K[u,kv] (f16 inputs, f32 accumulation and softmax, P
- * rounded to f16 for the P.V product).
+ * rounded to f16 for the P.V product; scale * log2(e) is folded into Q, each
+ * product rounded to f16 once, before the Q.K products).
  * Errors: TA_ERR_INVALID_ARGUMENT (null/misaligned pointer, plan not one-shot,
  * lse given without write_lse), TA_ERR_WORKSPACE, TA_ERR_HIP.
  */
