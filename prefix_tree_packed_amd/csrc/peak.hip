@@ -5,6 +5,10 @@
 // the 2.4 GHz that figure assumes). Every wave runs independent chains of
 // v_mfma_f32_16x16x32_f16 on register operands only (no memory traffic in the
 // loop), enough chains that each MFMA's latency is hidden behind the others.
+// Each chain has its own operands, pseudo-random f16 values in (-2, 2): under
+// load the MFMA rate of this part is power-limited, and near-constant
+// operands (little bit switching from one MFMA to the next) run measurably
+// faster than the data attention multiplies.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
@@ -19,16 +23,32 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 constexpr int kChains = 8;
 
 __global__ void __launch_bounds__(256) mfma_peak_kernel(int iters, float* __restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  // operands that depend on the lane so the compiler cannot fold the products
-  const h8 a = h8{} + (_Float16)(1.0f + lane * 1e-3f);
-  const h8 b = h8{} + (_Float16)(1.0f - lane * 1e-3f);
+  // per (chain, thread, element) operand values from an integer hash
+  // (a multiply-xorshift), mapped to (-2, 2)
+  auto rnd = [](unsigned x) {
+    x ^= x >> 16;
+    x *= 0x7feb352dU;
+    x ^= x >> 15;
+    x *= 0x846ca68bU;
+    x ^= x >> 16;
+    return (float)(x >> 8) * (4.0f / 16777216.0f) - 2.0f;
+  };
+  const unsigned seed = blockIdx.x * 256u + threadIdx.x;
+  h8 a[kChains], b[kChains];
   f4 acc[kChains];
 #pragma unroll
-  for (int c = 0; c < kChains; ++c) acc[c] = f4{0.f, 0.f, 0.f, (float)c};
+  for (int c = 0; c < kChains; ++c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[c][e] = (_Float16)rnd(seed * 131u + c * 16u + e);
+      b[c][e] = (_Float16)rnd(seed * 131u + c * 16u + 8u + e + 0x9e3779b9u);
+    }
+    acc[c] = f4{0.f, 0.f, 0.f, (float)c};
+  }
   for (int i = 0; i < iters; ++i) {
 #pragma unroll
-    for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
+    for (int c = 0; c < kChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[c], b[c], acc[c], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll
