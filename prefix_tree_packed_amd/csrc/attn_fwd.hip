@@ -694,7 +694,14 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
       // over the first tile that holds a key it sees
       refit(BoolC<false>{}, sa, sa);
     }
-    for (int kt = ktb; kt + 1 < kte; ++kt) {
+    // two steps per iteration, the score buffers swapping roles; an odd step
+    // count leaves the last scores in sb, copied once
+    int kt = ktb;
+    for (; kt + 2 < kte; kt += 2) {
+      step(kt, kte, sa, sb);
+      step(kt + 1, kte, sb, sa);
+    }
+    if (kt + 1 < kte) {
       step(kt, kte, sa, sb);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
