@@ -10,6 +10,10 @@ epilogue for the batch. The plan (host validation, token tables, block-sparse
 schedule, upload) is built once per batch before the timed region: it is
 shared by every layer of a model, and its host time is reported as
 plan_build_ms. Inputs are resident in HBM before timing starts.
+`ms_per_step` times the K steps with nothing between their launches (an
+event recorded between two launches leaves a gap of its own); the per-launch
+times (attention, cache write) come from K further steps with HIP events
+around each launch.
 
 By default the four 8192-token workloads (configs 1-4) are timed one after
 the other; the first (the Llama-8B-shaped forward) is the headline and the
@@ -216,13 +220,19 @@ def bench_config(cfg: int, args, dev, stream):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the K timed steps, with no events between their launches (an event
+    # record between launches leaves a gap of its own on the stream) ...
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for i in range(args.steps):
-        step(i)
+    for _ in range(args.steps):
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
+    # ... then K more with HIP events around each launch, for the per-launch times
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
     attn_ms = [[ev_a[i][j].elapsed_time(ev_b[i][j]) for j in range(n_fw)] for i in range(args.steps)]
     attn_ms = np.array(attn_ms)                       # [steps, forwards]
     attn_ms_mean = attn_ms.mean(axis=0)               # per forward
