@@ -547,15 +547,15 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   // tile kt+1 (K fragments read two sub-steps ahead, NCG MFMAs per fragment)
   // with the probabilities of tile kt spread between them, the reference
   // check of tile kt (a branch taken only when some probability reached the
-  // slack), then the P.V product of tile kt (V^T fragments read two
+  // slack), then the P.V product of tile kt (V^T fragments read three
   // sub-steps ahead). Fences keep the compiler from hoisting every LDS read
   // (which costs registers) or clustering the VALU work away from the MFMAs.
   // After the block, tile kt+1 is masked if flagged. No column max is taken
   // per tile: the check replaces it (about a quarter of the VALU work per step
   // before it). Tile kt+3's loads are issued at the start; K(kt+1) and V(kt)
-  // are read, so four stages keep every live tile resident. (Unrolling by two
-  // so the two score buffers swap roles instead of being copied runs out of
-  // registers; the copy mostly coalesces away.)
+  // are read, so four stages keep every live tile resident. The item loop
+  // runs two steps per iteration so that the two score buffers swap roles
+  // instead of being copied.
   constexpr int KPF = TA_KPF;                // K fragments read ahead of their S sub-step
   constexpr int VPF = TA_VPF;                // V^T fragments read ahead of their P.V sub-step
   static_assert(KPF >= 1 && VPF >= 1 && VPF <= 4 * DC, "read-ahead distances");
