@@ -172,7 +172,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
                         const _Float16* __restrict__ V, void* __restrict__ Out,
                         float* __restrict__ Lse, const QTile* __restrict__ qtiles,
                         const KTile* __restrict__ ktiles, const unsigned* __restrict__ mbits,
-                        const Seg* __restrict__ segs,
+                        const int* __restrict__ segs,
                         const int* __restrict__ wg_ptr, const int* __restrict__ wg_items,
                         int hq, int hkv, int n_q_total,
                         float scale_log2e) {
@@ -218,13 +218,13 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     vch[j] = 8 * ((lane % DCH) ^ v_swizzle<DCH>(row));
   }
 
-  // t: the tile's descriptor; sg: for a tile of several segments, segs[t.k0]
-  // .. segs[t.k0 + kMaxSegs] (header, then the segments), read ahead
-  auto issue = [&](int stage, int kvh, const KTile& t, const Seg (&sg)[kMaxSegs + 1]) {
+  // t: the tile's descriptor; sg: for a tile of several segments, its words
+  // of the packed segment table (kSegWords, see layout.h), read ahead
+  auto issue = [&](int stage, int kvh, const KTile& t, const int (&sg)[kSegWords]) {
     const int nk = t.meta & 0xffff;
     const int nseg = ((t.meta >> kSegShift) & (kMaxSegs - 1)) + 1;
-    // slot 0's row: k0 itself for a one-segment tile, else from the header
-    const int k0 = nseg > 1 ? sg[0].row0 : t.k0;
+    // slot 0's row: k0 itself for a one-segment tile, else from the table
+    const int k0 = nseg > 1 ? sg[0] : t.k0;
     const _Float16* kb = K + (size_t)kvh * D + (size_t)k0 * kv_stride;
     const _Float16* vb = V + (size_t)kvh * D + (size_t)k0 * kv_stride;
     // element offset of each loaded slot's row from slot 0's row: the slot
@@ -240,14 +240,15 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
       int rel[IPW];
 #pragma unroll
       for (int j = 0; j < IPW; ++j) rel[j] = lrow[j];
-      // segment k (k >= 1) is sg[1 + k]; segment 0 starts at slot 0, row k0
+      // segment k (k >= 1) is word k; segment 0 starts at slot 0, row k0
 #pragma unroll
       for (int k = 1; k < kMaxSegs; ++k) {
         if (k < nseg) {
-          const Seg x = sg[1 + k];
+          const unsigned x = (unsigned)sg[k];
+          const int slot0 = (int)(x & (kKeyTile - 1)), row0 = (int)(x >> kSegRowShift);
 #pragma unroll
           for (int j = 0; j < IPW; ++j)
-            rel[j] = lrow[j] >= x.slot0 ? x.row0 - k0 + (lrow[j] - x.slot0) : rel[j];
+            rel[j] = lrow[j] >= slot0 ? row0 - k0 + (lrow[j] - slot0) : rel[j];
         }
       }
 #pragma unroll
@@ -274,7 +275,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   // waited for at the start of a step.
   int l_pos = ib, l_kt = 0, l_kte = 0, l_kvh = 0, l_stage = 0;
   KTile l_desc{};
-  Seg l_sg[kMaxSegs + 1];
+  int l_sg[kSegWords];
   auto l_open = [&]() {
     const int w = wg_items[l_pos];
     const int qt = w / hkv;
@@ -287,7 +288,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     l_desc = ktiles[l_kt];
     if ((l_desc.meta >> kSegShift) & (kMaxSegs - 1)) {  // several segments
 #pragma unroll
-      for (int k = 0; k <= kMaxSegs; ++k) l_sg[k] = segs[l_desc.k0 + k];
+      for (int k = 0; k < kSegWords; ++k) l_sg[k] = segs[l_desc.k0 + k];
     }
   };
   l_open();
@@ -799,7 +800,7 @@ static hipError_t variant(const AttnArgs* a, hipStream_t st, int* per_cu) {
   hipLaunchKernelGGL(kernel, dim3(a->n_wg), dim3(WAVES * 64), 0, st, (const _Float16*)a->q,
                      (const _Float16*)a->k, (const _Float16*)a->v, a->o, a->lse,
                      (const QTile*)a->qtiles, (const KTile*)a->ktiles, (const unsigned*)a->mbits,
-                     (const Seg*)a->segs,
+                     (const int*)a->segs,
                      (const int*)a->wg_ptr,
                      (const int*)a->wg_items, a->hq, a->hkv, a->n_q,
                      a->scale_log2e);

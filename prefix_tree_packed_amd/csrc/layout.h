@@ -24,7 +24,7 @@ struct QTile {
 // 16 bits, in bit 16 whether the tile needs the per-element visibility test
 // (some key is not visible to every query of the tile, or the tile is short),
 // and nseg - 1 in bits 17-19. With one segment, slot s holds row-space key
-// k0 + s. With several, k0 is an index h into the segment table: segs[h] =
+// k0 + s. With several, k0 (host tables) is an index h into the segment table: segs[h] =
 // {first (P, E) entry of the tile's slots (host tables only), row of slot 0} and segs[h + 1 ..
 // h + nseg] are the segments (Seg below). `mblk` is the tile's block of
 // visibility bits (see mask_words_per_lane); unflagged tiles point at block 0, which
@@ -43,10 +43,21 @@ struct Seg {
   int32_t row0;
 };
 
+// The kernel's copy of the segments (device image): kSegWords 32-bit words per
+// multi-segment tile, whose device KTile::k0 is the index of its first word.
+// Word 0 is the row of slot 0; word k (1 <= k < nseg) is segment k packed as
+// slot0 | row0 << kSegRowShift (segment 0 starts at slot 0, row word 0). Half
+// the scalar registers of the header-and-segments form the kernel read ahead.
+constexpr int kSegWords = 8;
+constexpr int kSegRowShift = 6;
+
 constexpr int32_t kMaskedBit = 1 << 16;
 constexpr int kSegShift = 17;
 // A key tile lies on one root-to-leaf path, which has at most this many blocks.
 constexpr int kMaxSegs = 8;
+static_assert(kSegWords == kMaxSegs && (1 << kSegRowShift) == kKeyTile, "packed segment layout");
+// Row-space keys must fit the packed segment words.
+constexpr int64_t kRowSpaceLimit = int64_t(1) << (32 - kSegRowShift);
 
 // Persistent launch: at most this many workgroups, each walking its own list
 // of work items (query tile, KV head).

@@ -657,10 +657,23 @@ static void build_image(ta_plan_s* p) {
   off = align256(off + p->ktiles.size() * sizeof(KTile));
   p->off_mbits = off;
   off = align256(off + p->mbits.size() * sizeof(uint32_t));
-  // the kernel reads a multi-segment tile's header and kMaxSegs entries after
-  // it in one go: kMaxSegs zero entries of padding keep that in bounds
+  // the kernel's segment words: kSegWords per multi-segment tile, whose
+  // device copy's k0 points at them (layout.h)
+  std::vector<KTile> dkt(p->ktiles);
+  std::vector<uint32_t> dseg;
+  for (KTile& t : dkt) {
+    const int nseg = ((t.meta >> kSegShift) & (kMaxSegs - 1)) + 1;
+    if (nseg == 1) continue;
+    const size_t h = (size_t)t.k0;
+    t.k0 = (int32_t)dseg.size();
+    dseg.push_back((uint32_t)p->segs[h].row0);
+    for (int k = 1; k < kSegWords; ++k)
+      dseg.push_back(k < nseg ? (uint32_t)p->segs[h + 1 + k].slot0 |
+                                    ((uint32_t)p->segs[h + 1 + k].row0 << kSegRowShift)
+                              : 0u);
+  }
   p->off_segs = off;
-  off = align256(off + (p->segs.size() + kMaxSegs) * sizeof(Seg));
+  off = align256(off + std::max<size_t>(dseg.size(), 1) * sizeof(uint32_t));
   p->off_work = off;
   off = align256(off + p->work.size() * sizeof(int32_t));
   p->off_rowpos = off;
@@ -678,9 +691,9 @@ static void build_image(ta_plan_s* p) {
     if (n) memcpy(p->image.data() + o, src, n);
   };
   put(p->off_qtiles, p->qtiles.data(), p->qtiles.size() * sizeof(QTile));
-  put(p->off_ktiles, p->ktiles.data(), p->ktiles.size() * sizeof(KTile));
+  put(p->off_ktiles, dkt.data(), dkt.size() * sizeof(KTile));
   put(p->off_mbits, p->mbits.data(), p->mbits.size() * sizeof(uint32_t));
-  put(p->off_segs, p->segs.data(), p->segs.size() * sizeof(Seg));
+  put(p->off_segs, dseg.data(), dseg.size() * sizeof(uint32_t));
   put(p->off_work, p->work.data(), p->work.size() * sizeof(int32_t));
   put(p->off_rowpos, p->tok_rowpos.data(), p->tok_rowpos.size() * sizeof(int32_t));
   put(p->off_posid, p->pos_id.data(), p->pos_id.size() * sizeof(int32_t));
@@ -699,6 +712,9 @@ ta_status build_plan(const ta_tree_desc* desc, const ta_attn_cfg* cfg, ta_plan_s
   b.number_blocks();
   b.token_tables();
   if ((st = b.schedule()) != TA_OK) return st;
+  if (p->n_kv >= kRowSpaceLimit)
+    return fail(TA_ERR_LIMIT, "row space of %lld tokens; at most %lld", (long long)p->n_kv,
+                (long long)kRowSpaceLimit - 1);
   b.mask_bits();
   build_image(p);
   return TA_OK;
