@@ -53,6 +53,7 @@ typedef enum {
                                   misaligned buffer, call not valid for this plan      */
   TA_ERR_INVALID_TREE = 2,     /* empty row, block length < 1, parent not in [-1, self) */
   TA_ERR_LIMIT = 3,            /* row > 32768 tokens, forward > 8192 tokens, depth > 8,
+                                  rows' tokens together >= 2^26,
                                   head_dim not 64/128, heads per KV head not 1/2/4/8,
                                   readout model sizes outside their stated ranges       */
   TA_ERR_HIP = 4,              /* a HIP runtime call failed (message has its text)       */

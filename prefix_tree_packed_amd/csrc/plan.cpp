@@ -167,8 +167,10 @@ ta_status Builder::validate_and_layout() {
   if (q_off > kForwardLimit)
     return fail(TA_ERR_LIMIT, "forward computes %lld tokens > %lld", (long long)q_off,
                 (long long)kForwardLimit);
-  if (base > (int64_t)INT32_MAX - 2 * kRowLimit)
-    return fail(TA_ERR_LIMIT, "row space of %lld tokens does not fit 32-bit indexing", (long long)base);
+  // the kernel's packed segment words hold row-space indices in 26 bits
+  if (base >= kRowSpaceLimit)
+    return fail(TA_ERR_LIMIT, "row space of %lld tokens; at most %lld", (long long)base,
+                (long long)kRowSpaceLimit - 1);
   p->n_q = q_off;
   p->n_kv = base;
   p->num_rows = R;
@@ -712,9 +714,6 @@ ta_status build_plan(const ta_tree_desc* desc, const ta_attn_cfg* cfg, ta_plan_s
   b.number_blocks();
   b.token_tables();
   if ((st = b.schedule()) != TA_OK) return st;
-  if (p->n_kv >= kRowSpaceLimit)
-    return fail(TA_ERR_LIMIT, "row space of %lld tokens; at most %lld", (long long)p->n_kv,
-                (long long)kRowSpaceLimit - 1);
   b.mask_bits();
   build_image(p);
   return TA_OK;

@@ -400,6 +400,13 @@ def test_limits_and_invalid_trees(lib):
     assert _err(P.tree_attn_plan, bad_span, 4, 1, 64, 0.1) == 1
     bad_span2 = ok.with_q_range([0], [9])
     assert _err(P.tree_attn_plan, bad_span2, 4, 1, 64, 0.1) == 1
+    # the row space (all rows' tokens, cached ones included) stays below 2^26:
+    # 2048 full rows reach it, one query token each
+    n_rows = (1 << 26) // 32768
+    big = W.TreeDesc(np.arange(n_rows + 1, dtype=np.int32), np.full(n_rows, -1, np.int32),
+                     np.full(n_rows, 32768, np.int32), np.full(n_rows, 32767, np.int32),
+                     np.full(n_rows, 32768, np.int32))
+    assert _err(P.tree_attn_plan, big, 4, 1, 64, 0.1) == 3
 
 
 def test_head_config_errors(lib):
