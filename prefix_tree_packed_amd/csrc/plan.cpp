@@ -619,7 +619,9 @@ static ta_status check_cfg(const ta_attn_cfg* c) {
 
 // Persistent workgroups: longest-processing-time-first packing of the work
 // items (already in longest-first order) into n_wg lists, each item going to
-// the list with the least work so far (ties: lowest index). A workgroup's
+// the list with the least work so far (ties: lowest index), then a local
+// search that moves or swaps items out of the most loaded list while that
+// lowers it; each list runs its items longest first. A workgroup's
 // items cost their weighted key tiles plus about one tile of start-up. When
 // the KV heads and the workgroups both come in multiples of the XCD count,
 // the items of KV head h only go to workgroups w with w = h (mod XCDs): the
@@ -634,17 +636,74 @@ void assign_workgroups(const ta_plan_s* p, int n_wg, int32_t* wg_ptr, int32_t* w
   typedef std::pair<double, int32_t> Load;  // (work so far, workgroup)
   std::vector<std::priority_queue<Load, std::vector<Load>, std::greater<Load>>> heaps(classes);
   for (int w = 0; w < n_wg; ++w) heaps[w % classes].push({0.0, w});
+  auto cost = [&](int32_t item) { return 1.0 + p->item_cost[item / hkv]; };
+  std::vector<double> load(n_wg, 0.0);
   for (size_t i = 0; i < n; ++i) {
     const int32_t item = p->work[i];
     const int c = (item % hkv) % classes;
     Load l = heaps[c].top();
     heaps[c].pop();
     lists[l.second].push_back(item);
-    l.first += 1.0 + p->item_cost[item / hkv];
+    l.first += cost(item);
+    load[l.second] = l.first;
     heaps[c].push(l);
   }
+  // Local search after longest-first: while it lowers the largest load of a
+  // class, move an item of the class's most loaded workgroup to one of its
+  // least loaded ones, or swap it there for a smaller item. With few items
+  // per workgroup longest-first alone can leave the largest load well above
+  // the mean (a 6,255-token forward of short requests: 16% above, 3% after).
+  constexpr int kCand = 16;
+  std::vector<int> members, cand;
+  for (int c = 0; c < classes; ++c) {
+    members.clear();
+    for (int w = c; w < n_wg; w += classes) members.push_back(w);
+    const size_t max_moves = std::min<size_t>(4 * n / classes + 16, 4096);
+    for (size_t it = 0; it < max_moves; ++it) {
+      int b = members[0];
+      for (int w : members) b = load[w] > load[b] ? w : b;
+      cand = members;
+      const size_t k = std::min<size_t>(kCand, cand.size());
+      std::nth_element(cand.begin(), cand.begin() + (k - 1), cand.end(),
+                       [&](int x, int y) { return load[x] < load[y] || (load[x] == load[y] && x < y); });
+      cand.resize(k);
+      double best = 1e-9;
+      int bi = -1, bc = -1, bj = -1;
+      for (size_t ii = 0; ii < lists[b].size(); ++ii) {
+        const double ci = cost(lists[b][ii]);
+        for (int w : cand) {
+          if (w == b) continue;
+          const double mv = load[b] - std::max(load[b] - ci, load[w] + ci);
+          if (mv > best) best = mv, bi = (int)ii, bc = w, bj = -1;
+          for (size_t jj = 0; jj < lists[w].size(); ++jj) {
+            const double d = ci - cost(lists[w][jj]);
+            if (d <= 0) continue;
+            const double sw = load[b] - std::max(load[b] - d, load[w] + d);
+            if (sw > best) best = sw, bi = (int)ii, bc = w, bj = (int)jj;
+          }
+        }
+      }
+      if (bi < 0) break;
+      const int32_t x = lists[b][bi];
+      lists[b].erase(lists[b].begin() + bi);
+      load[b] -= cost(x);
+      if (bj >= 0) {
+        const int32_t y = lists[bc][bj];
+        lists[bc].erase(lists[bc].begin() + bj);
+        load[bc] -= cost(y);
+        lists[b].push_back(y);
+        load[b] += cost(y);
+      }
+      lists[bc].push_back(x);
+      load[bc] += cost(x);
+    }
+  }
+  // each list in longest-first (launch) order
+  std::vector<int32_t> rank(n > 0 ? (size_t)*std::max_element(p->work.begin(), p->work.end()) + 1 : 0);
+  for (size_t i = 0; i < n; ++i) rank[p->work[i]] = (int32_t)i;
   int32_t at = 0;
   for (int w = 0; w < n_wg; ++w) {
+    std::sort(lists[w].begin(), lists[w].end(), [&](int32_t x, int32_t y) { return rank[x] < rank[y]; });
     wg_ptr[w] = at;
     for (int32_t item : lists[w]) wg_items[at++] = item;
   }

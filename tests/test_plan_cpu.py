@@ -295,8 +295,9 @@ def test_tiles_by_prompt_position(lib, k):
 def test_workgroup_lists(lib, k):
     """The persistent split covers every work item exactly once, keeps the
     longest-first order inside each list, is balanced as longest-processing-
-    time packing guarantees (no list exceeds the mean load by more than one
-    item), and keeps each KV head on one XCD class when the counts allow."""
+    time packing guarantees (no list exceeds the mean load of its XCD class by
+    more than one item; the local search after it only lowers the largest
+    load), and keeps each KV head on one XCD class when the counts allow."""
     name, desc, hq, hkv, d = DESCS[k]
     plan = P.tree_attn_plan(desc, hq, hkv, d, d ** -0.5)
     sch = P.tree_attn_plan_schedule(plan)
@@ -320,6 +321,10 @@ def test_workgroup_lists(lib, k):
                 assert all((x % hkv) % 8 == w % 8 for x in lst)
         if not (hkv % 8 == 0 and n_wg % 8 == 0):
             assert max(loads) <= sum(loads) / n_wg + max(cost.values()) + 1e-9
+        else:
+            for c in range(8):
+                cls = loads[c::8]
+                assert max(cls) <= sum(cls) / len(cls) + max(cost.values()) + 1e-9
     # argument checks
     for bad in (0, -1, 8193):
         with pytest.raises(P.TreeAttnError):
