@@ -102,7 +102,7 @@ __device__ __forceinline__ float column_max(float x) {
 // before the S sub-step that uses them, V^T fragments VPF sub-steps before
 // their P.V sub-step.
 #ifndef TA_KPF
-#define TA_KPF 2
+#define TA_KPF 3
 #endif
 #ifndef TA_VPF
 #define TA_VPF 3
@@ -545,7 +545,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   };
 
   // Software pipeline. Step kt runs one hand-ordered block: the scores of
-  // tile kt+1 (K fragments read two sub-steps ahead, NCG MFMAs per fragment)
+  // tile kt+1 (K fragments read three sub-steps ahead, NCG MFMAs per fragment)
   // with the probabilities of tile kt spread between them, the reference
   // check of tile kt (a branch taken only when some probability reached the
   // slack), then the P.V product of tile kt (V^T fragments read three
