@@ -22,10 +22,10 @@
 //
 // The projections are skinny products (a few dozen rows against 14k-28k
 // weight rows), bound by streaming the weights once from HBM. A workgroup owns
-// 128 weight rows, 16 per wave, and runs v_mfma_f32_16x16x32_f16 with the
-// weight rows as the A operand (8 consecutive K values per lane, streamed from
-// global memory through a register ring several steps deep) and the
-// activation rows as the B operand (staged in LDS, shared by the eight waves).
+// 16 weight rows per wave (7 or 8 waves) and runs v_mfma_f32_16x16x32_f16 with
+// the weight rows as the A operand and the activation rows as the B operand,
+// both streamed from global memory straight into an LDS ring in whole row runs
+// and read from there as fragments.
 // Each output is one wave's MFMA chain over its K range (in an order fixed by
 // the output's column block), and the down product's K splits are fixed by
 // the weight shape and summed in split order, so nothing in a row's
@@ -44,7 +44,6 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kStepK = 64;  // K per pipeline step: two 32-deep MFMA slices
 
 __device__ __forceinline__ float wave_sum(float v) {
   // fixed butterfly: every lane ends with the same sum, in the same order
@@ -121,10 +120,11 @@ readout_norm_kernel(const _Float16* __restrict__ hidden, long long n_tokens,
   }
 }
 
-// One workgroup: WAVES * 16 weight rows, 16 per wave (one MFMA A fragment), against
-// one pass of MF*16 activation rows (the B fragments), over the K range
-// [split * k_len, (split + 1) * k_len). Every output is one wave's MFMA chain
-// over that range, 256-deep K stages starting at a stage fixed by the unit.
+// One workgroup: WAVES*16 weight rows, 16 per wave (one MFMA A fragment),
+// against one pass of MF*16 activation rows (the B fragments), over the K
+// range [split * k_len, (split + 1) * k_len). Every output is one wave's MFMA
+// chain over that range, in 256-deep blocks starting at a block fixed by the
+// unit.
 //   GATE_UP: w0 is the interleaved gate/up matrix (16-row blocks: gate rows
 //            8i .. 8i+7, then the up rows of the same columns); wave w streams
 //            block WAVES*unit + w, so its fragment rows 0-7 are gate rows
@@ -136,30 +136,87 @@ readout_norm_kernel(const _Float16* __restrict__ hidden, long long n_tokens,
 //            distance is unlucky).
 //   !GATE_UP: wave w's rows are w0 rows j0+16w .. j0+16w+15 (the down
 //            projection); output f32 partial[split][m][j0 .. j0+16*WAVES-1].
-// The activation rows of a 256-deep K slice are staged in LDS (two buffers,
-// shared by the waves); each wave streams its weight fragments through a
-// register ring kRing steps deep.
-constexpr int kSlice = 256;               // K per LDS stage
-constexpr int kSteps = kSlice / kStepK;   // pipeline steps per stage
-constexpr int kRingStages = 1;            // weight ring depth in LDS stages (1 or 2)
-constexpr int kRing = kRingStages * kSteps;  // weight steps in flight per wave
-constexpr int kRowB = kSlice * 2 + 16;    // LDS row stride in bytes (padded: conflict-free reads)
+//
+// Data movement. Weights and activations go from global memory straight into
+// an LDS ring of NS stages (global_load_lds_dwordx4), and the MFMA fragments
+// are read from there. A load-to-LDS instruction fills 1 KB of LDS in lane
+// order, but each lane picks its global address, so one instruction reads
+// whole row runs of SK*2 bytes (several 128-byte lines of a few rows) instead
+// of 64 bytes of each of a fragment's 16 rows, which is what reading fragments
+// straight into registers costs: a read-only probe of the two access patterns
+// over the Llama-8B shape's weights ran at 5.1 and 5.5 TB/s, 6.1 TB/s with
+// the weight loads marked nontemporal. The weight loads are nontemporal (read
+// once; without it this kernel ran no faster than the register form), the
+// activation loads are not (every workgroup of a pass re-reads them from L2).
+// Within a row the 16-byte chunks are
+// stored XOR-swizzled by the row (swz below), so that the 16 rows of a
+// fragment read the same logical chunk from distinct banks.
+//
+// Pipeline: stages s+1 .. s+NS-2 are in flight while stage s is computed. A
+// stage's loads are waited for by each wave (vmcnt; the loads are inline asm,
+// which the compiler neither counts nor waits for), then one barrier
+// publishes the stage to every wave and frees the buffer computed in the
+// previous stage, which the next stage's loads then refill.
+template <int MF, int SK, int NS, int WAVES>
+struct MlpCfg {
+  static constexpr int kWaves = WAVES;
+  static constexpr int kRows = MF * 16;           // activation rows per pass
+  static constexpr int kRowB = SK * 2;            // LDS bytes per row and stage
+  static constexpr int kCpr = SK / 8;             // 16-byte chunks per row
+  static constexpr int kRpi = 1024 / kRowB;       // rows per 1 KB load instruction
+  static constexpr int kRpb = 256 / kRowB;        // rows per 256 bytes of LDS (the bank period)
+  static constexpr int kWi = 16 / kRpi;           // weight loads per wave and stage
+  static constexpr int kXt = kRows / kRpi;        // activation loads per stage
+  static constexpr int kXi = (kXt + kWaves - 1) / kWaves;  // ... per wave
+  static constexpr int kP = kWi + kXi;            // loads per wave and stage
+  static constexpr int kWB = 16 * WAVES * kRowB;  // weight bytes per stage
+  static constexpr int kStageB = (16 * WAVES + kRows) * kRowB;
+  static constexpr int kDummyB = (kXi * kWaves - kXt) * 1024;  // unused activation load slots
+  static constexpr int kLdsB = NS * kStageB + kDummyB;
+  static_assert(SK == 64 || SK == 128, "stage depth");
+  static_assert(NS >= 2 && NS <= 4 && (NS - 2) * kP < 64, "ring depth");
+  static_assert(kLdsB <= 160 * 1024, "LDS");
+  // physical chunk of logical chunk c in LDS row r (r mod 16 is what matters)
+  static __device__ __forceinline__ int swz(int r) { return (r / kRpb) & (kCpr - 1); }
+};
 
-template <int MF>
-constexpr size_t mlp_lds_bytes() { return 2 * (size_t)MF * 16 * kRowB; }
+template <bool NT>
+__device__ __forceinline__ void mlp_dma16(const void* gptr, unsigned lds_addr) {
+  unsigned saved;
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %2, off nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr));
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr));
+}
 
-template <int MF, bool GATE_UP, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64)
+// s_waitcnt that waits until at most N vector-memory operations are
+// outstanding and leaves the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void mlp_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int MF, bool GATE_UP, int SK, int NS, int WAVES>
+__global__ void __launch_bounds__(512)
 mlp_mfma_kernel(const _Float16* __restrict__ x, int ldx,  // activations [n_rows, ldx]
                 const _Float16* __restrict__ w0, int ldw,
                 int n_rows, int k_len, int splits, int units, _Float16* __restrict__ act,
                 int ld_act, float* __restrict__ partial, int ld_part) {
-  __shared__ __attribute__((aligned(16))) unsigned char xs[mlp_lds_bytes<MF>()];  // [2][MF*16][kRowB]
-  constexpr int ROWS = MF * 16;
-  constexpr int NT = WAVES * 64;
-  constexpr int WROWS = WAVES * 16;                // weight rows per workgroup
-  constexpr int XCH = ROWS * (kSlice / 8) / NT;    // 16-byte chunks per thread per stage
-  static_assert(XCH >= 1 && ROWS * (kSlice / 8) % NT == 0, "activation stage split");
+  using C = MlpCfg<MF, SK, NS, WAVES>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kLdsB];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // A unit is (weight-row block, K split); each of its row passes is a
@@ -168,125 +225,123 @@ mlp_mfma_kernel(const _Float16* __restrict__ x, int ldx,  // activations [n_rows
   // so a weight tile streams from HBM once and its other passes hit L2.
   const int passes = gridDim.x / ((units + 7) / 8 * 8);
   const int unit = blockIdx.x / (8 * passes) * 8 + blockIdx.x % 8;
-  const int m0 = (blockIdx.x / 8) % passes * ROWS;
+  const int m0 = (blockIdx.x / 8) % passes * C::kRows;
   if (unit >= units) return;  // padding of the last group of 8 units
   const int split = unit % splits;
-  const int j0 = (unit / splits) * (GATE_UP ? WROWS / 2 : WROWS);
+  const int j0 = (unit / splits) * (GATE_UP ? 8 * WAVES : 16 * WAVES);
   const int kb = split * k_len;
-  const int nstages = k_len / kSlice;
-  const int nsteps = nstages * kSteps;
-  // Each unit walks its K range starting at its own stage and wrapping
-  // around: units that start together then read different K offsets of their
-  // rows instead of the same offset of rows a power-of-two stride apart, which
-  // piles the requests onto a few HBM channels (measured at d_model 8192: 13%
-  // faster). The order depends on the unit only, never on the rows in the call.
-  const int rot = (unit * 5) % nstages;
-  auto kstage = [&](int s) { return s + rot < nstages ? s + rot : s + rot - nstages; };
-  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int nstages = k_len / SK;
+  // Each unit walks its K range in 256-deep blocks starting at its own block
+  // and wrapping around: units that start together then read different K
+  // offsets of their rows instead of the same offset of rows a power-of-two
+  // stride apart, which piles the requests onto a few HBM channels (measured
+  // at d_model 8192). Stages run through a block in K order. The order of an
+  // output's MFMA chain therefore depends on the unit only, never on the stage
+  // depth or the rows in the call.
+  constexpr int kSpb = 256 / SK;  // stages per block
+  const int nblk = k_len / 256;
+  const int rot = (unit * 5) % nblk;
+  auto koff = [&](int s) {
+    const int b = s / kSpb + rot;
+    return (b < nblk ? b : b - nblk) * 256 + (s % kSpb) * SK;
+  };
 
-  // WROWS consecutive weight rows per workgroup, 16 per wave
-  const _Float16* wp = w0 + (size_t)(unit / splits * WROWS + 16 * wave + r16) * ldw + kb + kq;
-
-  {
-    // activation chunks this thread stages: chunk q = tid + i*256 -> row q / 32, 16 B column q % 32
-    const _Float16* xsrc[XCH];
-    int xdst[XCH];
+  // Load slots of this lane. Weight load i of wave w fills LDS rows
+  // 16w + i*kRpi .. (kRpi rows); lane l writes row 16w + i*kRpi + l / kCpr,
+  // physical chunk l % kCpr, which holds logical chunk (l % kCpr) ^ swz(row).
+  const _Float16* wsrc[C::kWi];
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int q = threadIdx.x + i * NT;
-      const int row = q >> 5, cc = q & 31;
-      xsrc[i] = x + (size_t)min(m0 + row, n_rows - 1) * ldx + kb + cc * 8;
-      xdst[i] = row * kRowB + cc * 16;
+  for (int i = 0; i < C::kWi; ++i) {
+    const int r = i * C::kRpi + lane / C::kCpr;
+    const int c = (lane % C::kCpr) ^ C::swz(r);
+    wsrc[i] = w0 + (size_t)(unit / splits * 16 * WAVES + 16 * wave + r) * ldw + kb + c * 8;
+  }
+  // Activation load j of wave w is load q = w + 8j of the stage (rows
+  // q*kRpi ..); slots past the stage's last load read a valid row into a
+  // dummy area, so every wave issues the same number of loads per stage.
+  const _Float16* xsrc[C::kXi];
+  unsigned xdst[C::kXi];
+#pragma unroll
+  for (int j = 0; j < C::kXi; ++j) {
+    const int q = wave + C::kWaves * j;
+    const int qq = q < C::kXt ? q : q - C::kXt;
+    const int r = qq * C::kRpi + lane / C::kCpr;
+    const int c = (lane % C::kCpr) ^ C::swz(r);
+    xsrc[j] = x + (size_t)min(m0 + r, n_rows - 1) * ldx + kb + c * 8;
+    xdst[j] = q < C::kXt ? C::kWB + qq * 1024 : NS * C::kStageB + (q - C::kXt) * 1024;
+  }
+  const unsigned lbase = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+  auto issue = [&](int s) {
+    const unsigned st = lbase + (s % NS) * C::kStageB;
+    const int ko = koff(s);
+#pragma unroll
+    for (int i = 0; i < C::kWi; ++i)
+      mlp_dma16<true>(wsrc[i] + ko, st + (16 * wave + i * C::kRpi) * C::kRowB);
+#pragma unroll
+    for (int j = 0; j < C::kXi; ++j) {
+      const bool dummy = wave + C::kWaves * j >= C::kXt;
+      mlp_dma16<false>(xsrc[j] + ko, (dummy ? lbase : st) + xdst[j]);
     }
-    // Activation stage s is loaded into register set s % 2 at the start of
-    // stage s - 2 and written to LDS buffer s % 2 at the end of stage s - 1.
-    // Loads complete in issue order, so waiting for it then also waits for the
-    // weight loads issued before it; loading two stages ahead keeps the weight
-    // loads of the last two stages in flight across every stage boundary.
-    h8 xr[2][XCH];
-    auto xload = [&](int set, int stage) {
-#pragma unroll
-      for (int i = 0; i < XCH; ++i) xr[set][i] = *(const h8*)(xsrc[i] + kstage(stage) * kSlice);
-    };
-    auto xstore = [&](int set, int buf) {
-#pragma unroll
-      for (int i = 0; i < XCH; ++i) *(h8*)(xs + buf * (ROWS * kRowB) + xdst[i]) = xr[set][i];
-    };
+  };
 
-    h8 wr[kRing][2];
-    auto wload = [&](int slot, int step) {
-      const int k = (kstage(step / kSteps) * kSteps + step % kSteps) * kStepK;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int sw = C::swz(r16);
+  f4 acc[MF];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) wr[slot][ks] = *(const h8*)(wp + k + ks * 32);
-    };
-    f4 acc[MF];
-#pragma unroll
-    for (int mf = 0; mf < MF; ++mf) acc[mf] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int mf = 0; mf < MF; ++mf) acc[mf] = f4{0.f, 0.f, 0.f, 0.f};
 
-    xload(0, 0);
-    xload(1, min(1, nstages - 1));
 #pragma unroll
-    for (int j = 0; j < kRing; ++j) wload(j, min(j, nsteps - 1));
-    xstore(0, 0);
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nstages) issue(s);
+  for (int s = 0; s < nstages; ++s) {
+    // stages issued after s and still allowed in flight
+    const int ahead = min(NS - 2, nstages - 1 - s);
+    if (ahead >= 2) mlp_wait_vmcnt<2 * C::kP>();
+    else if (ahead == 1) mlp_wait_vmcnt<C::kP>();
+    else mlp_wait_vmcnt<0>();
     __syncthreads();
-
-    for (int st = 0; st < nstages; st += 2) {
-      // two stages per iteration: register sets and ring slots are compile-time
+    if (s + NS - 1 < nstages) issue(s + NS - 1);
+    const unsigned char* wb = lds + (s % NS) * C::kStageB + (16 * wave + r16) * C::kRowB;
+    const unsigned char* xb = lds + (s % NS) * C::kStageB + C::kWB + r16 * C::kRowB;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int stage = st + half;
-        if (stage < nstages) {
-          xload(half, min(stage + 2, nstages - 1));  // past the end: re-read the last (L2 hit)
-          const unsigned char* xb = xs + half * (ROWS * kRowB);
-#pragma unroll
-          for (int j = 0; j < kSteps; ++j) {
-            const int slot = (half % kRingStages) * kSteps + j;
-            const int step = stage * kSteps + j;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-              for (int mf = 0; mf < MF; ++mf) {
-                const h8 b = *(const h8*)(xb + (mf * 16 + r16) * kRowB + (j * kStepK + ks * 32 + kq) * 2);
-                acc[mf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wr[slot][ks], b, acc[mf], 0, 0, 0);
-              }
-            }
-            // past the end the last step is re-read (an L2 hit) rather than branching
-            wload(slot, min(step + kRing, nsteps - 1));
-          }
-          xstore(half ^ 1, half ^ 1);
-          __syncthreads();
-        }
-      }
-    }
-
-    // D[n][m] of a fragment: lane (m % 16) + 16 * (n / 4), element n % 4
-    const int m = m0 + lane % 16;  // + 16 * mf
-    const int n4 = 4 * (lane >> 4);
-    if constexpr (GATE_UP) {
+    for (int sl = 0; sl < SK / 32; ++sl) {
+      const int off = ((sl * 4 + g) ^ sw) * 16;  // logical chunk sl*4 + g
+      const h8 a = *(const h8*)(wb + off);
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf) {
-        f4 up;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) up[e] = __shfl_xor(acc[mf][e], 32, 64);
-        if (lane < 32 && m + mf * 16 < n_rows) {
-          _Float16 q[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float g = (float)(_Float16)acc[mf][e];
-            const float u = (float)(_Float16)up[e];
-            q[e] = (_Float16)(g / (1.0f + expf(-g)) * u);
-          }
-          _Float16* dst = act + (size_t)(m + mf * 16) * ld_act + j0 + 8 * wave + n4;
-          *(uint2*)dst = *(const uint2*)q;
-        }
+        const h8 b = *(const h8*)(xb + mf * 16 * C::kRowB + off);
+        acc[mf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[mf], 0, 0, 0);
       }
-    } else {
-      float* dst = partial + (size_t)split * n_rows * ld_part;
-#pragma unroll
-      for (int mf = 0; mf < MF; ++mf)
-        if (m + mf * 16 < n_rows)
-          *(f4*)(dst + (size_t)(m + mf * 16) * ld_part + j0 + 16 * wave + n4) = acc[mf];
     }
+  }
+
+  // D[n][m] of a fragment: lane (m % 16) + 16 * (n / 4), element n % 4
+  const int m = m0 + lane % 16;  // + 16 * mf
+  const int n4 = 4 * (lane >> 4);
+  if constexpr (GATE_UP) {
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf) {
+      f4 up;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) up[e] = __shfl_xor(acc[mf][e], 32, 64);
+      if (lane < 32 && m + mf * 16 < n_rows) {
+        _Float16 q[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gt = (float)(_Float16)acc[mf][e];
+          const float u = (float)(_Float16)up[e];
+          q[e] = (_Float16)(gt / (1.0f + expf(-gt)) * u);
+        }
+        _Float16* dst = act + (size_t)(m + mf * 16) * ld_act + j0 + 8 * wave + n4;
+        *(uint2*)dst = *(const uint2*)q;
+      }
+    }
+  } else {
+    float* dst = partial + (size_t)split * n_rows * ld_part;
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+      if (m + mf * 16 < n_rows)
+        *(f4*)(dst + (size_t)(m + mf * 16) * ld_part + j0 + 16 * wave + n4) = acc[mf];
   }
 }
 
@@ -394,40 +449,65 @@ letter_logits_kernel(const _Float16* __restrict__ h, int dm, const _Float16* __r
   }
 }
 
-// Every pass runs 8 waves (128 weight rows) per workgroup, so each staged
-// activation row serves twice the weight bytes of a 4-wave workgroup (2-3%
-// faster at 14 and 64 rows than 4 waves). Up to 64 activation rows: one pass.
-// More: passes of 128 rows, so the weights stream once per 128 rows (135 KB of
-// LDS: one workgroup per CU). Each pass is a workgroup of its own.
+// 64-deep stages; four of them in the ring, three for 32-row passes (up to 32
+// rows the ring takes at most 78 KB of LDS, so two workgroups share a CU).
+// 128-deep stages and a three-stage ring ran at the same speed at 64 rows.
+// Above 64 rows the passes are 128 rows high, so the weights stream once per
+// 128 rows. Each pass is a workgroup of its own.
 template <int MF, bool GU, int WAVES>
 hipError_t launch_mlp(const _Float16* x, int ldx, const _Float16* w0, int ldw,
                       int n_rows, int k_len, int splits, int out_cols, _Float16* act,
                       int ld_act, float* partial, int ld_part, hipStream_t st) {
+  constexpr int kSK = 64, kNS = MF == 2 ? 3 : 4;
   const int n_col_blocks = out_cols / (GU ? 8 * WAVES : 16 * WAVES);
   const int units = n_col_blocks * splits;
   const int passes = (n_rows + MF * 16 - 1) / (MF * 16);
   const long long grid = (long long)(units + 7) / 8 * 8 * passes;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mlp_mfma_kernel<MF, GU, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64), 0, st,
-                     x, ldx, w0, ldw, n_rows, k_len, splits, units, act, ld_act, partial, ld_part);
+  if (k_len % 256 != 0 || k_len < 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((mlp_mfma_kernel<MF, GU, kSK, kNS, WAVES>), dim3((unsigned)grid),
+                     dim3(64 * WAVES), 0, st, x, ldx, w0, ldw, n_rows, k_len, splits, units, act,
+                     ld_act, partial, ld_part);
   return hipGetLastError();
 }
 
-template <bool GU>
+template <bool GU, int WAVES>
 hipError_t launch_mlp_rows(const _Float16* x, int ldx, const _Float16* w0, int ldw, int n_rows,
                            int k_len, int splits, int out_cols, _Float16* act, int ld_act,
                            float* partial, int ld_part, hipStream_t st) {
   if (n_rows <= 16)
-    return launch_mlp<1, GU, 8>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
-                                partial, ld_part, st);
+    return launch_mlp<1, GU, WAVES>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
+                                    partial, ld_part, st);
   if (n_rows <= 32)
-    return launch_mlp<2, GU, 8>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
-                                partial, ld_part, st);
+    return launch_mlp<2, GU, WAVES>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
+                                    partial, ld_part, st);
   if (n_rows <= 64)
-    return launch_mlp<4, GU, 8>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
+    return launch_mlp<4, GU, WAVES>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
+                                    partial, ld_part, st);
+  return launch_mlp<8, GU, WAVES>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
+                                  partial, ld_part, st);
+}
+
+// Waves (16 weight rows each) per gate/up workgroup, from the weight shape
+// alone (so the K order of every output, which follows the unit, never
+// depends on the rows in the call): 7 when 8 would leave fewer units than the
+// 256 CUs and 7 fill them, else 8. At the Llama-8B shape 8 waves leave 224
+// units and 32 CUs idle; 7 give 256 (gate/up 52 -> 40 us). At the 70B shape
+// (448 units of 8 waves) 7 waves were 1-2% slower.
+static int gate_up_waves(int d_ff) {
+  const int units8 = d_ff / 64;
+  return units8 < 256 && d_ff % 56 == 0 && d_ff / 56 >= 256 ? 7 : 8;
+}
+
+template <bool GU>
+hipError_t launch_mlp_shape(const _Float16* x, int ldx, const _Float16* w0, int ldw, int n_rows,
+                            int k_len, int splits, int out_cols, _Float16* act, int ld_act,
+                            float* partial, int ld_part, hipStream_t st) {
+  if (GU && gate_up_waves(out_cols) == 7)
+    return launch_mlp_rows<GU, 7>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
+                                  partial, ld_part, st);
+  return launch_mlp_rows<GU, 8>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
                                 partial, ld_part, st);
-  return launch_mlp<8, GU, 8>(x, ldx, w0, ldw, n_rows, k_len, splits, out_cols, act, ld_act,
-                              partial, ld_part, st);
 }
 
 // w_gate_up[16i + r] = w_gate[8i + r] (r < 8), w_up[8i + r - 8] (r >= 8); one
@@ -466,10 +546,10 @@ hipError_t launch_readout_mlp(const ReadoutArgs& a, hipStream_t st) {
                      (const int*)a.readout_tok, (const _Float16*)a.norm_w, dm, a.eps, xn);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_mlp_rows<true>(xn, dm, (const _Float16*)a.w_gate_up, dm, n, dm, 1, ff, act, ff,
+  e = launch_mlp_shape<true>(xn, dm, (const _Float16*)a.w_gate_up, dm, n, dm, 1, ff, act, ff,
                             nullptr, 0, st);
   if (e != hipSuccess) return e;
-  e = launch_mlp_rows<false>(act, ff, (const _Float16*)a.w_down, ff, n, ff / a.splits, a.splits, dm,
+  e = launch_mlp_shape<false>(act, ff, (const _Float16*)a.w_down, ff, n, ff / a.splits, a.splits, dm,
                              nullptr, 0, a.partial, dm, st);
   if (e != hipSuccess) return e;
   const long long units = (long long)n * (dm / 8);

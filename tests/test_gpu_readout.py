@@ -221,6 +221,36 @@ def test_batch_invariance(P):
             assert np.array_equal(a, b), f"{what} differs with the batch"
 
 
+def test_batch_invariance_llama8b_shape(P):
+    """At the Llama-8B shape the gate/up workgroups run 7 waves (256 units of
+    56 outputs; the small shapes above run 8): a row's act and h_out are
+    bitwise the same alone, in passes of 16, 32 and 64 rows and in two passes
+    of 128 rows, at different positions."""
+    dims = WR.LLAMA_8B
+    dm, ff, n_tok = dims["d_model"], dims["d_ff"], 256
+    print("[readout batch invariance] llama8b", flush=True)
+    inp = WR.draw(6, n_tok, [0], dm, ff, vocab=64, letters=2)
+    d = {k: _dev(getattr(inp, k)) for k in ("hidden", "norm_w", "w_down")}
+    d["w_gate_up"] = P.readout_pack_gate_up(_dev(inp.w_gate), _dev(inp.w_up))
+
+    def mlp(rows):
+        tok = torch.tensor(rows, dtype=torch.int32, device="cuda")
+        h = torch.empty((len(rows), dm), dtype=torch.float16, device="cuda")
+        ws = P.readout_mlp(d["hidden"], tok, d["norm_w"], d["w_gate_up"], d["w_down"], h, eps=inp.eps)
+        torch.cuda.synchronize()
+        _, act = P.readout_workspace_views(ws, len(rows), dm, ff)
+        return act.cpu().numpy(), h.cpu().numpy()
+
+    target = 77
+    act0, h0 = mlp([target])
+    assert np.isfinite(h0).all()
+    for n, pos in ((16, 9), (32, 31), (64, 0), (200, 141)):
+        rows = [(target if i == pos else (i * 37) % n_tok) for i in range(n)]
+        act, h = mlp(rows)
+        assert np.array_equal(act[pos], act0[0]), f"act differs in a batch of {n}"
+        assert np.array_equal(h[pos], h0[0]), f"h_out differs in a batch of {n}"
+
+
 @pytest.mark.parametrize("shape", ["llama8b", "llama70b"])
 def test_full_size(P, shape):
     """The Llama-8B shape with 64 readout rows of 4 letters (every column), and
