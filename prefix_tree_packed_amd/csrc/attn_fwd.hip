@@ -641,19 +641,13 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   int s = 0;  // stage of the tile being consumed
   // The end of every consumed tile: the tile two places further on must have
   // landed (only the one just issued may still be in flight) and every wave
-  // must be done with this tile's stage before it is refilled.
-  // The previous item's output stores (NST of them on every path, issued
-  // after its last barrier) sit between the tile loads of the first step of
-  // an item and the loads before them, so that step's wait lets them stay in
-  // flight too instead of draining them.
-  constexpr int NST = (OUT_F32 ? NCG * DT : NCG * DT / 2) + (LSE ? NCG : 0);
-  static_assert(LOADS + NST < 64, "vmcnt range");
-  bool stores_in_flight = false;
+  // must be done with this tile's stage before it is refilled. (The previous
+  // item's output stores, issued before the first tile loads of an item, are
+  // waited for by the first step of the item.)
+  static_assert(LOADS < 64 && NCG * DC < 64, "vmcnt range");
   auto end_of_tile = [&](bool issued) {
     if (!issued) wait_vmcnt<0>();
-    else if (stores_in_flight) wait_vmcnt<LOADS + NST>();
     else wait_vmcnt<LOADS>();
-    stores_in_flight = false;
     __syncthreads();
     s = (s + 1) & (kStages - 1);
   };
@@ -673,10 +667,18 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
   };
 
   f4 sa[4][NCG], sb[4][NCG];
+  bool deferred = false;  // the previous item's last step left its tile loads to this item
   for (int pos = ib;;) {
     // ---- item `pos`: Q fragments and columns are loaded -------------------
     const int ktb = tile.kt_begin, kte = tile.kt_end;
     scale_q();
+    if (deferred) {
+      // the loads the previous item's last step left; they go out after the
+      // previous item's output stores, so the first step's wait covers those
+      issue_next();
+      l_fetch();
+      deferred = false;
+    }
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
       mrun[cg] = 0.f;
@@ -711,22 +713,26 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     }
 
     // ---- the item's last tile: its scores are done, so Q is free ----------
-    // The next item's Q loads go out before this step's tile loads, so the
-    // end-of-tile wait (only the tile loads just issued may be outstanding)
-    // also covers them, and the output stores go out after that wait and the
-    // barrier, so neither waits for the stores to drain.
+    // The next item's Q loads go out here; this step's tile loads are deferred
+    // to the next item's start, after the compiler's wait for those Q loads,
+    // which would otherwise also wait for them (loads complete in issue order
+    // and the compiler does not count the inline-asm ones). The end-of-tile
+    // wait lets only the Q loads stay in flight; the output stores go out
+    // after it and the barrier, so nothing waits for them to drain.
     const int o_q_fwd = tile.q_fwd, o_n_tok = tile.n_tok, o_kvh = c_kvh;
     const bool last = pos + 1 >= ie;
     if (!last) open_item(pos + 1);
-    const bool issued = issue_next();
-    l_fetch();
     {
       h8 pb[2][NCG];
       probs(sa, pb);
       check_reference(BoolC<false>{}, sa, pb, sa);
       pv_product(s, pb);
     }
-    if (!last) end_of_tile(issued);
+    if (!last) {
+      wait_vmcnt<NCG * DC>();
+      __syncthreads();
+      s = (s + 1) & (kStages - 1);
+    }
     // Output of the finished item. A padded column (token >= n_tok) mirrors
     // the tile's last token with head (column mod G), so it computed exactly
     // what that real column computed and stores the same bytes to the same
@@ -770,7 +776,7 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
     if (last) break;
     // the stores above stay ahead of the next item's tile loads
     asm volatile("" ::: "memory");
-    stores_in_flight = true;
+    deferred = true;
     ++pos;
   }
 }
