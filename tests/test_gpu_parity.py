@@ -298,16 +298,18 @@ def _oracle_every_token(f, wl, block=512):
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_full_size_every_token(P, cfg):
     """Every token and head of the full-size workloads (seed 0), in the launch
-    configuration the bench times, element by element against the oracle; the
-    32k-token row streams its four chunks (later chunks over the cached K/V of
-    earlier ones)."""
+    configuration the bench times (f16 output, no LSE: the kernel instance the
+    bench launches, on the device-sized grid), element by element against the
+    oracle; the 32k-token row streams its four chunks (later chunks over the
+    cached K/V of earlier ones). The LSE instance is checked at full size on
+    sampled tokens above."""
     print(f"[full, every token] config {cfg}", flush=True)
     wl = W.make_config(cfg, 0)
-    outs, lses, _, _ = run_forwards(P, wl, out_dtype="f16", lse=True)
-    for j, (f, o, l) in enumerate(zip(wl.forwards, outs, lses)):
-        want, want_lse = _oracle_every_token(f, wl)
+    outs, lses, _, _ = run_forwards(P, wl, out_dtype="f16", lse=False)
+    assert all(l is None for l in lses)
+    for j, (f, o) in enumerate(zip(wl.forwards, outs)):
+        want, _ = _oracle_every_token(f, wl)
         err, rel = _compare(o, want, what=f"O forward {j}")
-        _compare(l, want_lse, atol=_lse_atol(f, wl), rl2=LSE_RL2, what=f"LSE forward {j}")
         print(f"[full, every token] config {cfg} forward {j}: {o.shape[0]} tokens, "
               f"max-abs {err:.2e}, rel-L2 {rel:.2e}", flush=True)
 
