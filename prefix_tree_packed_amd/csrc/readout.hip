@@ -148,9 +148,9 @@ readout_norm_kernel(const _Float16* __restrict__ hidden, long long n_tokens,
 // the weight loads marked nontemporal. The weight loads are nontemporal (read
 // once; without it this kernel ran no faster than the register form), the
 // activation loads are not (every workgroup of a pass re-reads them from L2).
-// Within a row the 16-byte chunks are
-// stored XOR-swizzled by the row (swz below), so that the 16 rows of a
-// fragment read the same logical chunk from distinct banks.
+// Within a row the 16-byte chunks are stored XOR-swizzled by the row (swz
+// below), so that the 16 rows of a fragment read the same logical chunk from
+// distinct banks.
 //
 // Pipeline: stages s+1 .. s+NS-2 are in flight while stage s is computed. A
 // stage's loads are waited for by each wave (vmcnt; the loads are inline asm,
