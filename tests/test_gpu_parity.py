@@ -295,22 +295,23 @@ def _oracle_every_token(f, wl, block=512):
     return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res], axis=1)
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-def test_full_size_every_token(P, cfg):
-    """Every token and head of the full-size workloads (seed 0), in the launch
-    configuration the bench times (f16 output, no LSE: the kernel instance the
-    bench launches, on the device-sized grid), element by element against the
+@pytest.mark.parametrize("cfg,seed", [(1, 0), (2, 0), (3, 0), (4, 0), (2, 1), (4, 1), (4, 2)])
+def test_full_size_every_token(P, cfg, seed):
+    """Every token and head of the full-size workloads (seed 0, and other
+    request mixes and random trees at seeds 1-2), in the launch configuration
+    the bench times (f16 output, no LSE: the kernel instance the bench
+    launches, on the device-sized grid), element by element against the
     oracle; the 32k-token row streams its four chunks (later chunks over the
     cached K/V of earlier ones). The LSE instance is checked at full size on
     sampled tokens above."""
-    print(f"[full, every token] config {cfg}", flush=True)
-    wl = W.make_config(cfg, 0)
+    print(f"[full, every token] config {cfg} seed {seed}", flush=True)
+    wl = W.make_config(cfg, seed)
     outs, lses, _, _ = run_forwards(P, wl, out_dtype="f16", lse=False)
     assert all(l is None for l in lses)
     for j, (f, o) in enumerate(zip(wl.forwards, outs)):
         want, _ = _oracle_every_token(f, wl)
         err, rel = _compare(o, want, what=f"O forward {j}")
-        print(f"[full, every token] config {cfg} forward {j}: {o.shape[0]} tokens, "
+        print(f"[full, every token] config {cfg} seed {seed} forward {j}: {o.shape[0]} tokens, "
               f"max-abs {err:.2e}, rel-L2 {rel:.2e}", flush=True)
 
 
