@@ -315,6 +315,19 @@ def test_full_size_every_token(P, cfg, seed):
               f"max-abs {err:.2e}, rel-L2 {rel:.2e}", flush=True)
 
 
+def test_full_size_every_token_f32_lse(P):
+    """The f32-output kernel instance with LSE on every token of config[1]:
+    O element by element at the attention bar, LSE within its bound."""
+    print("[full, every token] config 1 f32 + LSE", flush=True)
+    wl = W.make_config(1, 0)
+    outs, lses, _, _ = run_forwards(P, wl, out_dtype="f32", lse=True)
+    f, o, l = wl.forwards[0], outs[0], lses[0]
+    want, want_lse = _oracle_every_token(f, wl)
+    err, rel = _compare(o, want, what="O (f32)")
+    _compare(l, want_lse, atol=_lse_atol(f, wl), rl2=LSE_RL2, what="LSE")
+    print(f"[full, every token] config 1 f32: max-abs {err:.2e}, rel-L2 {rel:.2e}", flush=True)
+
+
 # ---------------------------------------------------------------------------
 # decision epilogue
 # ---------------------------------------------------------------------------
