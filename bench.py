@@ -37,6 +37,11 @@ timed region right after idle measures the ramp (config[1] attention ran
 beside the published peak; `attention_ms_p10_p50_p90` spreads the timed
 launches; `roofline.per_launch.algorithmic_gbps` and `kv_stream_gbps_per_forward`
 give the byte rates (the bound that matters for short-block workloads).
+`latency` gives the launch-latency-bound parts in microseconds: the small
+144-token workload (config[0]: cache write + attention) and the decision
+epilogue (config[0]'s one decision and the headline workload's batch), each
+per call over calls back to back and alone (the median of single calls
+between two events, which includes the events' own gaps).
 """
 from __future__ import annotations
 
@@ -110,6 +115,8 @@ def parse():
                     help="skip measuring the MFMA rate the device reaches (register-only loop)")
     ap.add_argument("--no-readout", action="store_true",
                     help="skip timing the readout-only last layer (MLP block and letter logits)")
+    ap.add_argument("--no-latency", action="store_true",
+                    help="skip timing the launch-latency-bound parts (config[0], decisions)")
     ap.add_argument("--device-warmup-ms", type=float, default=100.0,
                     help="before the W warm-up steps, run steps until this much wall time of "
                          "sustained load has passed: the device needs about 30 ms of load to "
@@ -400,6 +407,8 @@ def main():
 
     if not args.no_readout:
         out["readout"] = bench_readout(args, wl, plans, dev, stream)
+    if not args.no_latency:
+        out["latency"] = bench_latency(args, wl, dev, stream)
     if not args.no_mfma_probe:
         probe = mfma_attainable(dev, stream, args.device_warmup_ms)
         probe["attention_pct_of_attainable"] = round(100 * res["roofline"]["achieved"] / probe["tflops"], 2)
@@ -420,6 +429,65 @@ def main():
                 _, wlc, _, infc = results[c]
                 out["configs"][f"config[{c}]"]["cpu_baseline"] = cpu_baseline(wlc, infc, args.cpu_seconds / 2)
     print(json.dumps(out), flush=True)
+
+
+def bench_latency(args, wl_head, dev, stream):
+    """Microseconds per call of the launch-latency-bound parts: config[0]'s
+    forward (cache write + attention, 144 tokens) and decision epilogue, and
+    the headline workload's decision epilogue; back to back (K calls between
+    two events) and alone (median of single calls between two events)."""
+    import torch
+    import prefix_tree_packed_amd as P
+    from workloads import make_config
+
+    def T(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    wl = make_config(0, args.seed)
+    f = wl.forwards[0]
+    p = P.tree_attn_plan(f.tree, wl.hq, wl.hkv, wl.d, wl.scale, out_dtype=args.out_dtype)
+    P.tree_attn_plan_upload(p)
+    kn, vn = f.kv_new()
+    kc, vc = f.cache_before()
+    q, kn, vn, kc, vc = (T(a) for a in (f.q, kn, vn, kc, vc))
+    odt = torch.float16 if args.out_dtype == "f16" else torch.float32
+    o = torch.empty((p.info["num_q_tokens"], wl.hq, wl.d), dtype=odt, device=dev)
+
+    def decisions(d):
+        args_ = [T(d.logits), T(d.row1), T(d.row2), T(d.n_letters), T(d.T)]
+        pa = torch.empty((d.n_dec, d.logits.shape[1]), dtype=torch.float32, device=dev)
+        pc = torch.empty_like(pa)
+        return lambda: P.decision_readout(*args_, pa, pc, stream=stream)
+
+    def forward():
+        P.tree_attn_cache_write(p, kn, vn, kc, vc, stream=stream)
+        P.tree_attn_forward_cached(p, q, kc, vc, o, stream=stream)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps=200, alone_reps=50):
+        device_warmup(fn, 20.0)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        b2b = e0.elapsed_time(e1) * 1e3 / reps
+        ts = []
+        for _ in range(alone_reps):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return {"us_back_to_back": round(b2b, 2), "us_alone_median": round(float(np.median(ts)), 2)}
+
+    return {"config[0]_forward": dict(timed(forward), tokens=int(p.info["num_q_tokens"]),
+                                       launches="cache write + attention"),
+            "config[0]_decisions": dict(timed(decisions(wl.decisions)), decisions=int(wl.decisions.n_dec)),
+            "headline_decisions": dict(timed(decisions(wl_head.decisions)),
+                                       decisions=int(wl_head.decisions.n_dec))}
 
 
 def mfma_attainable(dev, stream, warmup_ms):
