@@ -269,7 +269,9 @@ tree_attn_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict_
 
   // Load cursor: the workgroup's key tiles as one sequence over its items.
   // Every tile consumed issues the tile three places further on (which may
-  // belong to a later item), so item boundaries do not drain the pipeline.
+  // belong to a later item), so item boundaries do not drain the pipeline
+  // (an item's last tile issues its loads at the next item's start instead,
+  // after the wait for that item's Q fragments).
   // The descriptor (and segment block) of the cursor's next tile is read one
   // step ahead, at the end of the previous step, so the scalar loads are not
   // waited for at the start of a step.
